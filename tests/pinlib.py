@@ -1,0 +1,178 @@
+"""Independent test-side formulations used to pin the oracle (not imported by the oracle or the
+GPU path). Everything here is written from the definitions, in a different form from the oracle:
+brute force over candidate sets, exact rational arithmetic, and a vectorised decoder of the
+documented pool layout.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from sparse_kv_cache_magnitude_amd.synth import bf16_to_f32
+
+
+def mag(bits) -> Fraction:
+    """Exact |x| of one bf16 bit pattern."""
+    return Fraction(abs(float(bf16_to_f32(np.uint16(bits)))))
+
+
+def kept_pair_brute(x4) -> tuple:
+    """The pair of positions whose magnitudes have the largest sum; among equal sums the
+    lexicographically smallest pair (itertools.combinations yields pairs in that order)."""
+    best, best_s = None, None
+    for pair in itertools.combinations(range(4), 2):
+        s = mag(x4[pair[0]]) + mag(x4[pair[1]])
+        if best is None or s > best_s:
+            best, best_s = pair, s
+    return best
+
+
+def fixed24(bits) -> int:
+    """floor(|x| * 2^24) in exact integer arithmetic."""
+    return math.floor(mag(bits) * (1 << 24))
+
+
+def groups_of_block(X, is_v, B, D, i):
+    """Yield (row, g, x4) for every 2:4 group of block i of one head X [L][D]."""
+    blk = X[i * B:(i + 1) * B]
+    if not is_v:
+        for t in range(B):
+            for g in range(D // 4):
+                yield t, g, blk[t, 4 * g:4 * g + 4]
+    else:
+        for c in range(D):
+            for g in range(B // 4):
+                yield c, g, blk[4 * g:4 * g + 4, c]
+
+
+def block_keys_exact(Kh, Vh, B, D):
+    """[nb][3] Python ints: K 2:4 loss, V 2:4 loss, whole-block loss (all of K and V)."""
+    nb = Kh.shape[0] // B
+    out = []
+    for i in range(nb):
+        k2 = v2 = p = 0
+        for is_v, X in ((0, Kh), (1, Vh)):
+            for _, _, x4 in groups_of_block(X, is_v, B, D, i):
+                keep = kept_pair_brute(x4)
+                for j in range(4):
+                    q = fixed24(x4[j])
+                    p += q
+                    if j not in keep:
+                        if is_v:
+                            v2 += q
+                        else:
+                            k2 += q
+        out.append((k2, v2, p))
+    return out
+
+
+def lowest_set(keys, candidates, n):
+    """The n-subset of candidates with the smallest key sum; ties -> lexicographically smallest
+    sorted tuple (combinations of a sorted list come in that order)."""
+    best, best_s = (), None
+    for comb in itertools.combinations(sorted(candidates), n):
+        s = sum(keys[i] for i in comb)
+        if best_s is None or s < best_s:
+            best, best_s = comb, s
+    return set(best)
+
+
+def modes_brute(keys, n_p, n_sk, n_sv):
+    """Block modes (0 pruned, 1 dense, 2 2:4) of one head from its exact keys, by enumeration."""
+    nb = len(keys)
+    pruned = lowest_set([k[2] for k in keys], range(nb), n_p)
+    surv = [i for i in range(nb) if i not in pruned]
+    sk = lowest_set([k[0] for k in keys], surv, n_sk)
+    sv = lowest_set([k[1] for k in keys], surv, n_sv)
+    mk = [0 if i in pruned else (2 if i in sk else 1) for i in range(nb)]
+    mv = [0 if i in pruned else (2 if i in sv else 1) for i in range(nb)]
+    return mk, mv
+
+
+def decode_cache(b, hkv, L, D, B, cache):
+    """Vectorised decoder of the documented layout: returns Kt, Vt [b][hkv][L][D] bf16 bits,
+    visible [b][hkv][nb], and kept masks (True where an element survives) for K and V."""
+    nb = L // B
+    mk = np.asarray(cache["map_k"]).reshape(b, hkv, nb)
+    mv = np.asarray(cache["map_v"]).reshape(b, hkv, nb)
+    kd = np.asarray(cache["k_dense"]).reshape(-1, B, D)
+    kn = np.asarray(cache["k_nnz"]).reshape(-1, B, D // 4, 2)
+    km = np.asarray(cache["k_meta"]).reshape(-1, B, D // 16)
+    vd = np.asarray(cache["v_dense"]).reshape(-1, D, B)
+    vn = np.asarray(cache["v_nnz"]).reshape(-1, D, B // 4, 2)
+    vm = np.asarray(cache["v_meta"]).reshape(-1, D, B // 16)
+    Kt = np.zeros((b, hkv, L, D), np.uint16)
+    Vt = np.zeros_like(Kt)
+    keepK = np.zeros(Kt.shape, bool)
+    keepV = np.zeros(Kt.shape, bool)
+
+    def nibbles(meta, ngroups):
+        g = np.arange(ngroups)
+        w = meta[..., g // 4].astype(np.int64)
+        return (w >> (4 * (g % 4))) & 0xF
+
+    for bi in range(b):
+        for h in range(hkv):
+            for i in range(nb):
+                sl = slice(i * B, (i + 1) * B)
+                x = mk[bi, h, i]
+                if x > 0:
+                    Kt[bi, h, sl] = kd[x - 1]
+                    keepK[bi, h, sl] = True
+                elif x < 0:
+                    nib = nibbles(km[-x - 1], D // 4)            # [B][D/4]
+                    blk = np.zeros((B, D // 4, 4), np.uint16)
+                    kb = np.zeros((B, D // 4, 4), bool)
+                    np.put_along_axis(blk, (nib & 3)[..., None], kn[-x - 1][..., 0:1], axis=2)
+                    np.put_along_axis(blk, (nib >> 2)[..., None], kn[-x - 1][..., 1:2], axis=2)
+                    np.put_along_axis(kb, (nib & 3)[..., None], True, axis=2)
+                    np.put_along_axis(kb, (nib >> 2)[..., None], True, axis=2)
+                    Kt[bi, h, sl] = blk.reshape(B, D)
+                    keepK[bi, h, sl] = kb.reshape(B, D)
+                y = mv[bi, h, i]
+                if y > 0:
+                    Vt[bi, h, sl] = vd[y - 1].T
+                    keepV[bi, h, sl] = True
+                elif y < 0:
+                    nib = nibbles(vm[-y - 1], B // 4)            # [D][B/4]
+                    blk = np.zeros((D, B // 4, 4), np.uint16)
+                    kb = np.zeros((D, B // 4, 4), bool)
+                    np.put_along_axis(blk, (nib & 3)[..., None], vn[-y - 1][..., 0:1], axis=2)
+                    np.put_along_axis(blk, (nib >> 2)[..., None], vn[-y - 1][..., 1:2], axis=2)
+                    np.put_along_axis(kb, (nib & 3)[..., None], True, axis=2)
+                    np.put_along_axis(kb, (nib >> 2)[..., None], True, axis=2)
+                    Vt[bi, h, sl] = blk.reshape(D, B).T
+                    keepV[bi, h, sl] = kb.reshape(D, B).T
+    vis = (mk != 0).astype(np.uint8)
+    return Kt, Vt, vis, keepK, keepV
+
+
+def attention_full_matrix(Q, Kt, Vt, vis, B, causal, scale=None):
+    """Eq. (1) with the full score matrix materialised (no online softmax), fp64.
+    Q [b][hq][lq][D]; Kt, Vt [b][hkv][L][D] bf16 bits; returns O [b][hq][lq][D], lse."""
+    q = bf16_to_f32(Q).astype(np.float64)
+    k = bf16_to_f32(Kt).astype(np.float64)
+    v = bf16_to_f32(Vt).astype(np.float64)
+    b, hq, lq, D = q.shape
+    hkv, L = k.shape[1], k.shape[2]
+    G = hq // hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    O = np.zeros((b, hq, lq, D))
+    lse = np.full((b, hq, lq), -np.inf)
+    tok_vis = np.repeat(vis.astype(bool), B, axis=2)          # [b][hkv][L]
+    for bi in range(b):
+        for h in range(hq):
+            S = q[bi, h] @ k[bi, h // G].T * scale              # [lq][L]
+            allowed = np.broadcast_to(tok_vis[bi, h // G], S.shape).copy()
+            if causal:
+                allowed &= np.arange(L)[None, :] <= np.arange(lq)[:, None]
+            S = np.where(allowed, S, -np.inf)
+            for r in range(lq):
+                if not allowed[r].any():
+                    continue
+                m = S[r].max()
+                w = np.exp(S[r] - m)
+                O[bi, h, r] = w @ v[bi, h // G] / w.sum()
+                lse[bi, h, r] = m + math.log(w.sum())
+    return O, lse

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against what the paper and the mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: brute-force enumeration, exact
+rational arithmetic, the paper's printed worked values (tests/golden), a library routine
+(torch scaled_dot_product_attention in float64), or an identity that holds exactly.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Dims
+from sparse_kv_cache_magnitude_amd import synth
+from tests import pinlib
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hierasparse_worked_values.json")
+
+
+def tie_heavy(shape, seed):
+    """bf16 bits drawn from a tiny value set so that equal magnitudes are common."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 3.0], np.float32)
+    return synth.bf16_bits(vals[rng.integers(0, len(vals), size=shape)])
+
+
+def normal(shape, seed):
+    return synth.bf16_bits(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))
+
+
+# ------------------------------------------------------------------------------------------------
+# C1: element selection (Eq. 2a-2b, fused top-2 of §IV-B)
+
+@pytest.mark.parametrize("maker", [tie_heavy, normal])
+def test_kept_pairs_match_brute_force(maker):
+    d = Dims(b=1, hkv=2, L=32, D=32, B=16, n_p=0, n_sk=2, n_sv=2)   # every block 2:4
+    K = maker((d.b, d.hkv, d.L, d.D), 1)
+    V = maker((d.b, d.hkv, d.L, d.D), 2)
+    cache = oracle.compress(d, K, V)
+    _, _, _, keepK, keepV = pinlib.decode_cache(d.b, d.hkv, d.L, d.D, d.B, cache)
+    for h in range(d.hkv):
+        for is_v, X, keep in ((0, K[0, h], keepK[0, h]), (1, V[0, h], keepV[0, h])):
+            for i in range(d.nb):
+                for row, g, x4 in pinlib.groups_of_block(X, is_v, d.B, d.D, i):
+                    if not is_v:
+                        got = keep[i * d.B + row, 4 * g:4 * g + 4]
+                    else:
+                        got = keep[i * d.B + 4 * g:i * d.B + 4 * g + 4, row]
+                    want = pinlib.kept_pair_brute(x4)
+                    assert tuple(np.flatnonzero(got)) == want, (h, is_v, i, row, g, x4)
+
+
+def test_exactly_two_kept_and_magnitude_order():
+    d = Dims(b=2, hkv=1, L=64, D=64, B=32, n_p=0, n_sk=2, n_sv=2)
+    K = normal((d.b, d.hkv, d.L, d.D), 3)
+    V = tie_heavy((d.b, d.hkv, d.L, d.D), 4)
+    cache = oracle.compress(d, K, V)
+    Kt, Vt, _, keepK, keepV = pinlib.decode_cache(d.b, d.hkv, d.L, d.D, d.B, cache)
+    # K groups: 4 consecutive channels; V groups: 4 consecutive tokens
+    gk = keepK.reshape(d.b, d.hkv, d.L, d.D // 4, 4)
+    gv = keepV.reshape(d.b, d.hkv, d.L // 4, 4, d.D)
+    assert (gk.sum(-1) == 2).all() and (gv.sum(-2) == 2).all()
+    ak = np.abs(synth.bf16_to_f32(K)).reshape(gk.shape)
+    av = np.abs(synth.bf16_to_f32(V)).reshape(gv.shape)
+    kept_min = np.where(gk, ak, np.inf).min(-1)
+    drop_max = np.where(~gk, ak, -np.inf).max(-1)
+    assert (kept_min >= drop_max).all()
+    kept_min = np.where(gv, av, np.inf).min(-2)
+    drop_max = np.where(~gv, av, -np.inf).max(-2)
+    assert (kept_min >= drop_max).all()
+    # kept values are the input values, dropped ones read back as zero
+    assert (Kt == np.where(keepK, K, 0)).all() and (Vt == np.where(keepV, V, 0)).all()
+
+
+# ------------------------------------------------------------------------------------------------
+# C2-C3: block losses (Eq. 2c) and block modes (Eq. 2d + pruned state)
+
+def test_block_keys_exact_arithmetic():
+    d = Dims(b=1, hkv=2, L=64, D=16, B=16, n_p=1, n_sk=1, n_sv=2)
+    K = tie_heavy((d.b, d.hkv, d.L, d.D), 5)
+    V = normal((d.b, d.hkv, d.L, d.D), 6)
+    V[0, 1, 5, 3] = synth.bf16_bits(np.float32(3e-6))   # below 2^-17: truncated by the key
+    V[0, 1, 6, 3] = synth.bf16_bits(np.float32(1e-30))
+    out = oracle.compress(d, K, V, with_loss=True)
+    for h in range(d.hkv):
+        want = pinlib.block_keys_exact(K[0, h], V[0, h], d.B, d.D)
+        got = [tuple(int(x) for x in row) for row in out["keys"][0, h]]
+        assert got == want
+        # the fp64 L1 sums are the exact losses up to rounding
+        exact = []
+        for i in range(d.nb):
+            row = []
+            for is_v, X in ((0, K[0, h]), (1, V[0, h])):
+                s = 0
+                for _, _, x4 in pinlib.groups_of_block(X, is_v, d.B, d.D, i):
+                    keep = pinlib.kept_pair_brute(x4)
+                    s += sum(pinlib.mag(x4[j]) for j in range(4) if j not in keep)
+                row.append(float(s))
+            exact.append(row)
+        np.testing.assert_allclose(out["loss"][0, h, :, :2], np.array(exact), rtol=1e-13)
+
+
+@pytest.mark.parametrize("counts", [(0, 3, 5), (2, 3, 4), (3, 5, 0), (8, 0, 0), (0, 8, 8),
+                                    (1, 7, 7)])
+def test_block_modes_brute_force(counts):
+    n_p, n_sk, n_sv = counts
+    d = Dims(b=2, hkv=2, L=8 * 16, D=16, B=16, n_p=n_p, n_sk=n_sk, n_sv=n_sv)
+    K = tie_heavy((d.b, d.hkv, d.L, d.D), 7)
+    V = tie_heavy((d.b, d.hkv, d.L, d.D), 8)
+    # duplicate some blocks so whole-block and 2:4 keys tie exactly
+    K[:, :, 16:32] = K[:, :, 48:64]
+    V[:, :, 16:32] = V[:, :, 48:64]
+    K[:, :, 96:112] = K[:, :, 0:16]
+    V[:, :, 96:112] = V[:, :, 0:16]
+    out = oracle.compress(d, K, V)
+    mk = out["map_k"].reshape(d.b, d.hkv, d.nb)
+    mv = out["map_v"].reshape(d.b, d.hkv, d.nb)
+    for bi in range(d.b):
+        for h in range(d.hkv):
+            keys = [tuple(int(x) for x in r) for r in out["keys"][bi, h]]
+            want_k, want_v = pinlib.modes_brute(keys, n_p, n_sk, n_sv)
+            got_k = [0 if x == 0 else (1 if x > 0 else 2) for x in mk[bi, h]]
+            got_v = [0 if x == 0 else (1 if x > 0 else 2) for x in mv[bi, h]]
+            assert got_k == want_k and got_v == want_v
+
+
+def test_fp64_loss_ranking_agrees_with_integer_keys():
+    w = synth.workload("decode_llama8b_32k_b8")
+    d = Dims(b=1, hkv=2, L=8192, D=128, B=64, n_p=19, n_sk=77, n_sv=77)
+    K, V = synth.make_kv(w.seed, 1, 2, d.L, d.D, outliers=4)
+    out = oracle.compress(d, K, V, with_loss=True)
+    for h in range(2):
+        for j in range(3):
+            ki = np.lexsort((np.arange(d.nb), out["keys"][0, h, :, j]))
+            kf = np.lexsort((np.arange(d.nb), out["loss"][0, h, :, j]))
+            assert (ki == kf).all()
+
+
+# ------------------------------------------------------------------------------------------------
+# C4-C5: index map and pools
+
+def test_round_trip_and_map_is_a_bijection():
+    d = Dims(b=2, hkv=3, L=256, D=32, B=32, n_p=2, n_sk=3, n_sv=4)
+    K = normal((d.b, d.hkv, d.L, d.D), 9)
+    V = normal((d.b, d.hkv, d.L, d.D), 10)
+    cache = oracle.compress(d, K, V)
+    Kt, Vt, vis, keepK, keepV = pinlib.decode_cache(d.b, d.hkv, d.L, d.D, d.B, cache)
+    # unpack(pack(X)) = X on kept elements and 0 elsewhere, bit for bit
+    assert (Kt == np.where(keepK, K, 0)).all() and (Vt == np.where(keepV, V, 0)).all()
+    # dense blocks keep everything, pruned blocks nothing, 2:4 blocks exactly half
+    nb = d.nb
+    mk = cache["map_k"].reshape(d.b, d.hkv, nb)
+    mv = cache["map_v"].reshape(d.b, d.hkv, nb)
+    kb = keepK.reshape(d.b, d.hkv, nb, -1).mean(-1)
+    vb = keepV.reshape(d.b, d.hkv, nb, -1).mean(-1)
+    assert (kb == np.where(mk > 0, 1.0, np.where(mk < 0, 0.5, 0.0))).all()
+    assert (vb == np.where(mv > 0, 1.0, np.where(mv < 0, 0.5, 0.0))).all()
+    assert ((mk == 0) == (mv == 0)).all() and ((mk == 0).sum(-1) == d.n_p).all()
+    # every pool slot is used exactly once, and a head's slots increase with block index
+    for m, n_s in ((mk, d.n_sk), (mv, d.n_sv)):
+        n_d = nb - d.n_p - n_s
+        for bi in range(d.b):
+            for h in range(d.hkv):
+                head = bi * d.hkv + h
+                dense = m[bi, h][m[bi, h] > 0]
+                sparse = -m[bi, h][m[bi, h] < 0]
+                assert list(dense) == list(range(head * n_d + 1, head * n_d + n_d + 1))
+                assert list(sparse) == list(range(head * n_s + 1, head * n_s + n_s + 1))
+    # the oracle's own decompression agrees with the test-side decoder
+    Kt2, Vt2, vis2 = oracle.unpack(d, cache)
+    assert (Kt2 == Kt).all() and (Vt2 == Vt).all() and (vis2 == vis).all()
+
+
+def test_rejects_out_of_range_inputs():
+    d = Dims(b=1, hkv=1, L=16, D=16, B=16, n_p=0, n_sk=1, n_sv=0)
+    K = np.zeros((1, 1, 16, 16), np.uint16)
+    V = K.copy()
+    K[0, 0, 3, 3] = synth.bf16_bits(np.float32(2.0 ** 24))
+    with pytest.raises(ValueError):
+        oracle.compress(d, K, V)
+    K[0, 0, 3, 3] = 0x7F80  # +inf
+    with pytest.raises(ValueError):
+        oracle.compress(d, K, V)
+    with pytest.raises(ValueError):
+        oracle.compress(Dims(1, 1, 16, 16, 16, 1, 1, 0), K * 0, V)   # n_p + n_sk > nb
+
+
+# ------------------------------------------------------------------------------------------------
+# Sizes: Eq. (4)-(6), Table V
+
+def _bytes_no_prune(L, D, B, n_sk, n_sv):
+    return oracle.pool_bytes(Dims(1, 1, L, D, B, 0, n_sk, n_sv))
+
+
+@pytest.mark.parametrize("L,B,SK,SV", [(4096, 64, 0.5, 1.0), (4096, 64, 1.0, 1.0),
+                                       (8192, 128, 0.25, 0.75), (2048, 16, 0.0, 1.0)])
+def test_byte_count_equals_closed_form(L, B, SK, SV):
+    D = 128
+    nb = L // B
+    n_sk, n_sv = int(SK * nb), int(SV * nb)
+    got = _bytes_no_prune(L, D, B, n_sk, n_sv)
+    e = 2  # bytes per element
+    size_den = e * (L * D * (1 - SK) + L * D * (1 - SV))        # Eq. (5b)
+    size_nnz = e * (0.5 * L * D * SK + 0.5 * L * D * SV)         # Eq. (5c)
+    size_e = e * (L * D * SK / 16 + L * D * SV / 16)             # Eq. (5d)
+    size_idx = 4 * 2 * L / B                                      # Eq. (5a), int32 entries
+    assert got["k_dense"] + got["v_dense"] == size_den
+    assert got["k_nnz"] + got["v_nnz"] == size_nnz
+    assert got["k_meta"] + got["v_meta"] == size_e
+    assert got["map_k"] + got["map_v"] == size_idx
+
+
+def test_eq6_worked_compression_ratios():
+    g = json.load(open(GOLDEN))["compression_ratio_eq6"]
+    L, D, B = 32768, 128, 64
+    nb = L // B
+    for case in g["cases"]:
+        got = _bytes_no_prune(L, D, B, int(case["S_K"] * nb), int(case["S_V"] * nb))
+        r = 2 * L * D * 2 / sum(got.values())                    # Eq. (3)-(4)
+        assert f"{r:.2f}" == f"{case['r_comp']:.2f}"
+
+
+def test_table_v_memory_column():
+    g = json.load(open(GOLDEN))["table_v_key_value_memory_gib"]
+    for row in g["rows"]:
+        L = row["context"]
+        per_head = _bytes_no_prune(L, g["head_dim"], 64, L // 64, 0)
+        scale = g["layers"] * g["kv_heads"] / 2 ** 30
+        dense = per_head["v_dense"] * scale
+        sparse = (per_head["k_nnz"] + per_head["k_meta"]) * scale
+        assert f"{dense:.2f}" == f"{row['dense']:.2f}"
+        assert f"{sparse:.2f}" == f"{row['sparse_S1']:.2f}"
+
+
+# ------------------------------------------------------------------------------------------------
+# C7-C8: attention (Eq. 1)
+
+def _sdpa(q, k, v, causal, G):
+    q = torch.from_numpy(synth.bf16_to_f32(q).astype(np.float64))
+    k = torch.from_numpy(synth.bf16_to_f32(k).astype(np.float64)).repeat_interleave(G, dim=1)
+    v = torch.from_numpy(synth.bf16_to_f32(v).astype(np.float64)).repeat_interleave(G, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparsity_zero_equals_library_attention(causal):
+    d = Dims(b=2, hkv=2, L=128, D=32, B=16, n_p=0, n_sk=0, n_sv=0)
+    hq = 8
+    K = normal((d.b, d.hkv, d.L, d.D), 11)
+    V = normal((d.b, d.hkv, d.L, d.D), 12)
+    cache = oracle.compress(d, K, V)
+    lq = d.L if causal else 1
+    Q = normal((d.b, hq, lq, d.D), 13)
+    if causal:
+        O, _ = oracle.prefill(d, cache, Q)
+    else:
+        O, _ = oracle.decode(d, cache, Q, hq)
+    want = _sdpa(Q, K, V, causal, hq // d.hkv)
+    np.testing.assert_allclose(O.reshape(want.shape), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("counts", [(0, 2, 2), (1, 1, 0), (1, 0, 1)])
+def test_brute_force_tiny_heads(causal, counts):
+    d = Dims(b=1, hkv=1, L=32, D=16, B=16, n_p=counts[0], n_sk=counts[1], n_sv=counts[2])
+    hq = 2
+    K = normal((1, 1, d.L, d.D), 14)
+    V = normal((1, 1, d.L, d.D), 15)
+    cache = oracle.compress(d, K, V)
+    Kt, Vt, vis, _, _ = pinlib.decode_cache(1, 1, d.L, d.D, d.B, cache)
+    Q = normal((1, hq, d.L if causal else 1, d.D), 16)
+    want, want_lse = pinlib.attention_full_matrix(Q, Kt, Vt, vis, d.B, causal)
+    if causal:
+        O, lse = oracle.prefill(d, cache, Q)
+    else:
+        O, lse = oracle.decode(d, cache, Q, hq)
+    np.testing.assert_allclose(O.reshape(want.shape), want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse.reshape(want_lse.shape), want_lse, rtol=0, atol=1e-12)
+
+
+def test_special_cases():
+    D, B, L = 16, 16, 64
+    d = Dims(1, 1, L, D, B, 0, 0, 0)
+    K = normal((1, 1, L, D), 17)
+    row = normal((D,), 18)
+    V = np.broadcast_to(row, (1, 1, L, D)).copy()
+    cache = oracle.compress(d, K, V)
+    # all value rows equal -> the output is that row
+    O, _ = oracle.decode(d, cache, normal((1, 1, D), 19), 1)
+    np.testing.assert_allclose(O[0], synth.bf16_to_f32(row), atol=1e-12)
+    # q = 0 -> uniform weights -> mean of the visible value rows
+    d2 = Dims(1, 1, L, D, B, 1, 1, 1)
+    V2 = normal((1, 1, L, D), 20)
+    cache2 = oracle.compress(d2, K, V2)
+    Kt, Vt, vis, _, _ = pinlib.decode_cache(1, 1, L, D, B, cache2)
+    O, lse = oracle.decode(d2, cache2, np.zeros((1, 1, D), np.uint16), 1)
+    tok = np.repeat(vis[0, 0].astype(bool), B)
+    np.testing.assert_allclose(O[0], synth.bf16_to_f32(Vt[0, 0][tok]).astype(np.float64).mean(0),
+                               atol=1e-12)
+    assert abs(lse[0] - math.log(tok.sum())) < 1e-12
+    # a single visible token -> its value row (prefill row 0 sees only token 0)
+    O, lse = oracle.prefill(d, cache, normal((1, 1, L, D), 21), rows=[0])
+    np.testing.assert_allclose(O[0], synth.bf16_to_f32(V[0, 0, 0]), atol=1e-12)
+    # everything pruned -> zero output, lse = -inf
+    d3 = Dims(1, 1, L, D, B, L // B, 0, 0)
+    cache3 = oracle.compress(d3, K, V2)
+    O, lse = oracle.decode(d3, cache3, normal((1, 1, D), 22), 1)
+    assert (O == 0).all() and np.isneginf(lse).all()
+    O, lse = oracle.prefill(d3, cache3, normal((1, 1, L, D), 23))
+    assert (O == 0).all() and np.isneginf(lse).all()
+
+
+def test_dropped_mass_identity():
+    """Dropping tokens of softmax mass eps moves the output by exactly eps * (o_dropped - o_kept)
+    (Jet-QSparse, arXiv 2611.01022, §3.4 'Effect of omitted mass', Eq. 5), and by at most eps times
+    the diameter of the value set."""
+    D, B, L, hq = 32, 16, 256, 4
+    K = normal((1, 2, L, D), 24)
+    V = normal((1, 2, L, D), 25)
+    Q = normal((1, hq, 1, D), 26)
+    nb = L // B
+    kept = np.zeros((1, 2, nb), np.uint8)
+    kept[..., ::3] = 1
+    kept[..., 5] = 1
+    allv = np.ones_like(kept)
+    o_all, lse_all = oracle.attention(Q, K, V, allv, B, False)
+    o_kept, _ = oracle.attention(Q, K, V, kept, B, False)
+    o_drop, lse_drop = oracle.attention(Q, K, V, 1 - kept, B, False)
+    eps = np.exp(lse_drop - lse_all)[:, None]
+    np.testing.assert_allclose(o_all - o_kept, eps * (o_drop - o_kept), atol=1e-12)
+    vv = synth.bf16_to_f32(V).astype(np.float64)
+    for r in range(hq):
+        vals = vv[0, r // 2]
+        diam = max(np.linalg.norm(vals[i] - vals[j]) for i in range(0, L, 7) for j in range(L))
+        assert np.linalg.norm(o_all[r] - o_kept[r]) <= eps[r, 0] * diam + 1e-12
+    # and the compressed cache's pruned blocks behave exactly as those dropped tokens
+    d = Dims(1, 2, L, D, B, 6, 0, 0)
+    cache = oracle.compress(d, K, V)
+    vis = (cache["map_k"].reshape(1, 2, nb) != 0).astype(np.uint8)
+    o_c, _ = oracle.decode(d, cache, Q, hq)
+    o_v, _ = oracle.attention(Q, K, V, vis, B, False)
+    np.testing.assert_allclose(o_c, o_v, atol=1e-15)
+
+
+def test_split_merge_by_log_sum_exp():
+    """Partial outputs over a partition of the visible blocks, merged by their log-sum-exp, equal
+    the unsplit result (the combine step of the split-KV decode)."""
+    D, B, L, hq = 32, 16, 512, 4
+    K = normal((2, 1, L, D), 27)
+    V = normal((2, 1, L, D), 28)
+    Q = normal((2, hq, 1, D), 29)
+    nb = L // B
+    vis = np.ones((2, 1, nb), np.uint8)
+    vis[..., 3] = 0
+    o_full, lse_full = oracle.attention(Q, K, V, vis, B, False)
+    parts = []
+    for s in range(5):
+        m = np.zeros_like(vis)
+        m[..., s::5] = vis[..., s::5]
+        parts.append(oracle.attention(Q, K, V, m, B, False))
+    lses = np.stack([p[1] for p in parts])
+    mstar = lses.max(0)
+    w = np.exp(lses - mstar)
+    o = sum(w[i][:, None] * parts[i][0] for i in range(5)) / w.sum(0)[:, None]
+    np.testing.assert_allclose(o, o_full, atol=1e-12)
+    np.testing.assert_allclose(mstar + np.log(w.sum(0)), lse_full, atol=1e-12)
+
+
+def test_gqa_mapping():
+    D, B, L = 32, 16, 128
+    K = normal((1, 2, L, D), 30)
+    V = normal((1, 2, L, D), 31)
+    Q = normal((1, 8, 1, D), 32)
+    vis = np.ones((1, 2, L // B), np.uint8)
+    o, _ = oracle.attention(Q, K, V, vis, B, False)
+    # G = 4: query head h reads KV head h // 4, i.e. replicating KV heads gives the same result
+    Kr, Vr = np.repeat(K, 4, axis=1), np.repeat(V, 4, axis=1)
+    o_rep, _ = oracle.attention(Q, Kr, Vr, np.ones((1, 8, L // B), np.uint8), B, False)
+    np.testing.assert_allclose(o, o_rep, atol=0)
+    # G = 1 equals running each head on its own
+    for h in range(8):
+        oh, _ = oracle.attention(Q[:, h:h + 1], Kr[:, h:h + 1], Vr[:, h:h + 1],
+                                 np.ones((1, 1, L // B), np.uint8), B, False)
+        np.testing.assert_allclose(oh[0], o_rep[h], atol=0)
