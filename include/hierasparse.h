@@ -1,0 +1,153 @@
+/*
+ * hierasparse.h -- C ABI of libhierasparse.so: hierarchical semi-structured sparse KV attention
+ * on MI355X (gfx950).
+ *
+ * The operations follow "HieraSparse: Hierarchical Semi-Structured Sparse KV Attention"
+ * (arXiv 2604.16864v2, cited as [HS]):
+ *   hs_compress      [HS] §III-A Eq. (2a)-(2d) magnitude pruner + §III-B memory pools and signed
+ *                    block index map + §IV-B fused magnitude compression kernel.
+ *   hs_decode_attn   [HS] Eq. (1) over the compressed cache, §IV-C split-KV decode with a
+ *                    log-sum-exp combine step and GQA packing.
+ *   hs_prefill_attn  [HS] §III-C Algorithm 1 with the mixed dense/sparse dispatch of §III-C2,
+ *                    made causal, skipping pruned blocks.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
+ *   - Every pointer except the size-query outputs is a DEVICE pointer owned by the caller. The
+ *     library allocates no memory and keeps no state besides a thread-local error string.
+ *   - Work is enqueued asynchronously on 'stream' (a hipStream_t; NULL = the default stream).
+ *     Calls on different streams may run concurrently if their buffers do not overlap.
+ *   - All arguments are validated on the host before anything is launched. On any error the
+ *     call returns a non-zero hs_status, enqueues nothing, and hs_last_error() describes it.
+ *     Faults inside a launched kernel surface at the caller's next synchronisation.
+ *   - Inputs must be finite with |x| < 2^24 (the compressor's integer loss keys rely on it);
+ *     this is documented, not checked.
+ *   - GPU limits: head_dim = 128, block in {64, 128}, seq_len % block = 0,
+ *     seq_len / block <= 4096, q_heads % kv_heads = 0. Every pointer must be 16-byte aligned.
+ *
+ * Block modes and the compressed cache (per batch entry b and KV head h, independently)
+ *   The sequence is cut into nb = seq_len / block blocks. Each block is pruned (its tokens are
+ *   dropped from attention for K and V together), dense, or 2:4 (two of every four elements kept,
+ *   [HS] §III-A); K and V choose dense or 2:4 independently. K is 2:4 along head_dim (groups of four
+ *   consecutive channels of one token), V along tokens (four consecutive tokens of one channel):
+ *   each tensor is sparse along the reduction axis of the product that consumes it ([HS] §III-C1,
+ *   Table II, "Trans-Both").
+ *   Selection: the n_pruned blocks with the smallest sum of |x| over K and V are pruned; among the
+ *   rest, the n_sparse_k blocks with the smallest K 2:4 loss (sum of |x| of the dropped elements,
+ *   [HS] Eq. (2c)) become K 2:4, and likewise for V. Losses are compared as integer sums of
+ *   floor(|x| * 2^24); equal losses go to the lower block index. Within a group, the two largest
+ *   |x| are kept; equal magnitudes go to the lower position.
+ *
+ *   map_k, map_v   int32 [batch][kv_heads][nb]: 0 = pruned, +(i + 1) = dense slot i,
+ *                  -(i + 1) = 2:4 slot i. The slots of head (b, h) are the contiguous range
+ *                  (b * kv_heads + h) * count .. + count - 1, assigned in block order.
+ *   k_dense        [Nd_k][block][head_dim]      token-major copy of a K block
+ *   k_nnz          [Ns_k][block][head_dim / 2]  kept K values, two per group, in position order
+ *   k_meta         [Ns_k][block][head_dim / 16] 2-bit positions: group g of a token uses bits
+ *                                               4*(g%4)..4*(g%4)+3 of word g/4, first kept
+ *                                               position in the low two bits
+ *   v_dense        [Nd_v][head_dim][block]      channel-major copy of a V block
+ *   v_nnz          [Ns_v][head_dim][block / 2]  kept V values of each channel, two per group
+ *   v_meta         [Ns_v][head_dim][block / 16] positions, same packing over token groups
+ *   with Nd_x = batch * kv_heads * (nb - n_pruned - n_sparse_x), Ns_x = batch * kv_heads *
+ *   n_sparse_x. A 2:4 block costs (1/2 + 1/16) of a dense one, matching [HS] Eq. (5c)-(5d).
+ *
+ * GQA: query head hq reads KV head hq / (q_heads / kv_heads).
+ * A query with no visible token gets output 0 and log-sum-exp -inf.
+ */
+#ifndef HIERASPARSE_H
+#define HIERASPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_NULL = 1,        /* a required pointer is NULL */
+  HS_ERR_SHAPE = 2,       /* shape outside the supported set (see limits above) */
+  HS_ERR_COUNTS = 3,      /* negative counts or n_pruned + n_sparse_x > nb */
+  HS_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  HS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hs_workspace_size() */
+  HS_ERR_UNSUPPORTED = 6, /* valid request this build does not implement (e.g. flags) */
+  HS_ERR_HIP = 7          /* a HIP launch failed; hs_last_error() has the HIP message */
+} hs_status;
+
+typedef struct {
+  int32_t batch, q_heads, kv_heads;
+  int32_t seq_len;  /* tokens in the cache (decode) or in the prompt (prefill) */
+  int32_t head_dim; /* D */
+  int32_t block;    /* B, tokens per block */
+} hs_shape;
+
+/* Block counts per (batch entry, KV head); the same for every head. */
+typedef struct {
+  int32_t n_pruned, n_sparse_k, n_sparse_v;
+} hs_counts;
+
+typedef struct {
+  int32_t *map_k, *map_v;
+  uint16_t *k_dense, *k_nnz, *k_meta;
+  uint16_t *v_dense, *v_nnz, *v_meta;
+} hs_cache;
+
+typedef struct {
+  size_t map_k, map_v, k_dense, k_nnz, k_meta, v_dense, v_nnz, v_meta;
+} hs_cache_bytes;
+
+enum { HS_OP_COMPRESS = 1, HS_OP_DECODE = 2 };
+
+/* Prefill flags: how 2:4 blocks reach the matrix cores. */
+enum {
+  HS_PREFILL_SMFMAC = 0,    /* sparse MFMA (v_smfmac) on the packed values, the default */
+  HS_PREFILL_DECOMPRESS = 1 /* expand 2:4 blocks to dense in LDS, then dense MFMA */
+};
+
+/* Bytes of every buffer of the compressed cache for this shape and these counts (host call, no
+   GPU needed). A buffer of size 0 may be passed as NULL. */
+hs_status hs_cache_sizes(const hs_shape *shape, const hs_counts *counts, hs_cache_bytes *out);
+
+/* Workspace bytes needed by hs_compress (op = HS_OP_COMPRESS: three 8-byte loss keys per block)
+   or hs_decode_attn (op = HS_OP_DECODE: fp32 partial outputs and log-sum-exps of every split;
+   num_splits = 0 selects the same automatic split count hs_decode_attn uses). Host call. */
+hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *counts,
+                            int32_t num_splits, size_t *bytes);
+
+/* Compress K, V [batch][kv_heads][seq_len][head_dim] into 'out' (all eight buffers, sized by
+   hs_cache_sizes). 'ws' is device scratch of hs_workspace_size(HS_OP_COMPRESS) bytes. Deterministic:
+   the same input gives the same bytes. */
+hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
+                      const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Decode attention of one new query per (batch entry, query head) over all seq_len cached
+   tokens: q [batch][q_heads][head_dim] -> o [batch][q_heads][head_dim] (bf16), and if lse is not
+   NULL, lse [batch][q_heads] (fp32, natural log). softmax_scale <= 0 selects 1/sqrt(head_dim).
+   num_splits = 0 picks the split-KV factor automatically (1..512 otherwise). 'ws' is device
+   scratch of hs_workspace_size(HS_OP_DECODE, ..., num_splits) bytes. */
+hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts, const hs_cache *cache,
+                         const uint16_t *q, uint16_t *o, float *lse, float softmax_scale,
+                         int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Causal prefill attention: q [batch][q_heads][seq_len][head_dim] -> o (same shape, bf16) and,
+   if lse is not NULL, lse [batch][q_heads][seq_len]. Query position i attends the visible tokens
+   t <= i of the compressed cache of the same sequence. flags: HS_PREFILL_SMFMAC or
+   HS_PREFILL_DECOMPRESS. No workspace. */
+hs_status hs_prefill_attn(const hs_shape *shape, const hs_counts *counts, const hs_cache *cache,
+                          const uint16_t *q, uint16_t *o, float *lse, float softmax_scale,
+                          uint32_t flags, void *stream);
+
+/* Static description of a status code. */
+const char *hs_status_string(hs_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *hs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIERASPARSE_H */

@@ -1,0 +1,243 @@
+// hs_api.hip -- the C ABI of libhierasparse.so (declared in include/hierasparse.h).
+//
+// Host side only: validates every argument before anything is enqueued, computes buffer sizes,
+// and launches the gfx950 kernels of hs_compress.hip, hs_decode.hip and hs_prefill.hip on the
+// caller's stream. The library allocates nothing; all scratch comes from the caller.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "hierasparse.h"
+#include "hs_internal.h"
+
+#define HS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+hs_status fail(hs_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hs_status ok() {
+  g_error[0] = '\0';
+  return HS_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape and count rules shared by all entry points.
+hs_status make_dims(const hs_shape *s, const hs_counts *c, hs::Dims *d) {
+  if (!s || !c) return fail(HS_ERR_NULL, "shape or counts is NULL");
+  if (s->batch <= 0 || s->q_heads <= 0 || s->kv_heads <= 0 || s->seq_len <= 0)
+    return fail(HS_ERR_SHAPE, "batch, q_heads, kv_heads and seq_len must be positive");
+  if (s->q_heads % s->kv_heads)
+    return fail(HS_ERR_SHAPE, "q_heads (%d) must be a multiple of kv_heads (%d)", s->q_heads,
+                s->kv_heads);
+  if (s->head_dim != 128) return fail(HS_ERR_SHAPE, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->block != 64 && s->block != 128)
+    return fail(HS_ERR_SHAPE, "block must be 64 or 128 (got %d)", s->block);
+  if (s->seq_len % s->block)
+    return fail(HS_ERR_SHAPE, "seq_len (%d) must be a multiple of block (%d)", s->seq_len,
+                s->block);
+  const int nb = s->seq_len / s->block;
+  if (nb > hs::kMaxBlocks)
+    return fail(HS_ERR_SHAPE, "seq_len / block = %d exceeds %d blocks per head", nb,
+                hs::kMaxBlocks);
+  if ((int64_t)s->batch * s->kv_heads > 65535 || (int64_t)s->batch * s->q_heads > 65535)
+    return fail(HS_ERR_SHAPE, "batch * heads exceeds 65535");
+  if (c->n_pruned < 0 || c->n_sparse_k < 0 || c->n_sparse_v < 0)
+    return fail(HS_ERR_COUNTS, "block counts must be non-negative");
+  if (c->n_pruned + c->n_sparse_k > nb || c->n_pruned + c->n_sparse_v > nb)
+    return fail(HS_ERR_COUNTS, "n_pruned + n_sparse_{k,v} exceeds the %d blocks per head", nb);
+  d->b = s->batch;
+  d->hq = s->q_heads;
+  d->hkv = s->kv_heads;
+  d->G = s->q_heads / s->kv_heads;
+  d->L = s->seq_len;
+  d->D = s->head_dim;
+  d->B = s->block;
+  d->nb = nb;
+  d->np = c->n_pruned;
+  d->nsk = c->n_sparse_k;
+  d->nsv = c->n_sparse_v;
+  d->ndk = nb - c->n_pruned - c->n_sparse_k;
+  d->ndv = nb - c->n_pruned - c->n_sparse_v;
+  return HS_OK;
+}
+
+hs_cache_bytes cache_bytes(const hs::Dims &d) {
+  const size_t heads = (size_t)d.b * d.hkv, bd = (size_t)d.B * d.D;
+  hs_cache_bytes r;
+  r.map_k = r.map_v = heads * d.nb * sizeof(int32_t);
+  r.k_dense = heads * d.ndk * bd * 2;
+  r.k_nnz = heads * d.nsk * bd;          // bd / 2 values of 2 bytes
+  r.k_meta = heads * d.nsk * bd / 8;     // bd / 16 words of 2 bytes
+  r.v_dense = heads * d.ndv * bd * 2;
+  r.v_nnz = heads * d.nsv * bd;
+  r.v_meta = heads * d.nsv * bd / 8;
+  return r;
+}
+
+// The pointers of a cache: non-NULL and aligned wherever the buffer is non-empty.
+hs_status check_cache(const hs_cache *c, const hs::Dims &d, hs::CacheView *v) {
+  if (!c) return fail(HS_ERR_NULL, "cache is NULL");
+  const hs_cache_bytes n = cache_bytes(d);
+  const void *p[8] = {c->map_k, c->map_v, c->k_dense, c->k_nnz,
+                      c->k_meta, c->v_dense, c->v_nnz, c->v_meta};
+  const size_t sz[8] = {n.map_k, n.map_k, n.k_dense, n.k_nnz, n.k_meta, n.v_dense, n.v_nnz, n.v_meta};
+  static const char *names[8] = {"map_k", "map_v", "k_dense", "k_nnz",
+                                 "k_meta", "v_dense", "v_nnz", "v_meta"};
+  for (int i = 0; i < 8; ++i) {
+    if (sz[i] && !p[i]) return fail(HS_ERR_NULL, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(HS_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  *v = hs::CacheView{c->map_k, c->map_v, c->k_dense, c->k_nnz,
+                     c->k_meta, c->v_dense, c->v_nnz, c->v_meta};
+  return HS_OK;
+}
+
+hs_status check_ptr(const void *p, const char *name, bool required = true) {
+  if (!p) return required ? fail(HS_ERR_NULL, "%s is NULL", name) : HS_OK;
+  if (!aligned16(p)) return fail(HS_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return HS_OK;
+}
+
+// Split-KV factor of the decode: enough workgroups to cover the chip several times, with at
+// least four visible blocks per split.
+int auto_splits(const hs::Dims &d) {
+  const int heads = d.b * d.hkv;
+  const int visible = d.nb - d.np;
+  int s = (2048 + heads - 1) / heads;
+  int cap = (visible + 3) / 4;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  if (s > 512) s = 512;
+  return s;
+}
+
+size_t decode_ws_bytes(const hs::Dims &d, int splits) {
+  const size_t rows = (size_t)d.b * d.hq * splits;
+  return rows * d.D * sizeof(float) + rows * sizeof(float);
+}
+
+size_t compress_ws_bytes(const hs::Dims &d) { return (size_t)d.b * d.hkv * d.nb * 3 * sizeof(uint64_t); }
+
+float scale_log2(float softmax_scale, int D) {
+  float s = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  return s * 1.4426950408889634f;
+}
+
+}  // namespace
+
+HS_API hs_status hs_cache_sizes(const hs_shape *shape, const hs_counts *counts,
+                                hs_cache_bytes *out) {
+  hs::Dims d;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if (!out) return fail(HS_ERR_NULL, "out is NULL");
+  *out = cache_bytes(d);
+  return ok();
+}
+
+HS_API hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *counts,
+                                   int32_t num_splits, size_t *bytes) {
+  hs::Dims d;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if (!bytes) return fail(HS_ERR_NULL, "bytes is NULL");
+  if (op == HS_OP_COMPRESS) {
+    *bytes = compress_ws_bytes(d);
+  } else if (op == HS_OP_DECODE) {
+    if (num_splits < 0 || num_splits > 512)
+      return fail(HS_ERR_SHAPE, "num_splits must be in 0..512 (got %d)", num_splits);
+    *bytes = decode_ws_bytes(d, num_splits ? num_splits : auto_splits(d));
+  } else {
+    return fail(HS_ERR_UNSUPPORTED, "unknown op %d", op);
+  }
+  return ok();
+}
+
+HS_API hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
+                             const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  hs::Dims d;
+  hs::CacheView c;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v"))) return st;
+  if ((st = check_cache(out, d, &c))) return st;
+  if (!ws || ws_bytes < compress_ws_bytes(d))
+    return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", compress_ws_bytes(d),
+                ws_bytes, ws ? "" : ", NULL");
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  hipError_t e = hs::launch_compress(d, k, v, c, (uint64_t *)ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+HS_API hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts,
+                                const hs_cache *cache, const uint16_t *q, uint16_t *o, float *lse,
+                                float softmax_scale, int32_t num_splits, void *ws,
+                                size_t ws_bytes, void *stream) {
+  hs::Dims d;
+  hs::CacheView c;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if ((st = check_cache(cache, d, &c))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse", false)))
+    return st;
+  if (num_splits < 0 || num_splits > 512)
+    return fail(HS_ERR_SHAPE, "num_splits must be in 0..512 (got %d)", num_splits);
+  const int splits = num_splits ? num_splits : auto_splits(d);
+  const size_t need = decode_ws_bytes(d, splits);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                ws ? "" : ", NULL");
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  float *part_o = (float *)ws;
+  float *part_lse = part_o + (size_t)d.b * d.hq * splits * d.D;
+  hipError_t e = hs::launch_decode(d, c, q, o, lse, scale_log2(softmax_scale, d.D), splits, part_o,
+                                   part_lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+HS_API hs_status hs_prefill_attn(const hs_shape *shape, const hs_counts *counts,
+                                 const hs_cache *cache, const uint16_t *q, uint16_t *o, float *lse,
+                                 float softmax_scale, uint32_t flags, void *stream) {
+  hs::Dims d;
+  hs::CacheView c;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if ((st = check_cache(cache, d, &c))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse", false)))
+    return st;
+  if (flags != HS_PREFILL_SMFMAC && flags != HS_PREFILL_DECOMPRESS)
+    return fail(HS_ERR_UNSUPPORTED, "unknown prefill flags 0x%x", flags);
+  hipError_t e = hs::launch_prefill(d, c, q, o, lse, scale_log2(softmax_scale, d.D),
+                                    flags == HS_PREFILL_SMFMAC, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+HS_API const char *hs_status_string(hs_status s) {
+  switch (s) {
+    case HS_OK: return "ok";
+    case HS_ERR_NULL: return "null pointer";
+    case HS_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case HS_ERR_COUNTS: return "invalid block counts";
+    case HS_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case HS_ERR_WORKSPACE: return "workspace missing or too small";
+    case HS_ERR_UNSUPPORTED: return "unsupported request";
+    case HS_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+HS_API const char *hs_last_error(void) { return g_error; }

@@ -1,0 +1,303 @@
+// hs_compress.hip -- magnitude-based hierarchical compressor for gfx950.
+//
+// "HieraSparse" (arXiv 2604.16864v2) §III-A Eq. (2a)-(2d), §III-B memory pools / signed block
+// index map, §IV-B fused magnitude compression. Three kernels, all streaming K and V from HBM:
+//   k_score  one workgroup per (head, block): reads the K and V block once and reduces the three
+//            integer losses of the block (K 2:4 loss, V 2:4 loss, whole-block magnitude).
+//   k_rank   one workgroup per head: bitonic sorts of (loss, block index) in LDS choose the pruned,
+//            K 2:4 and V 2:4 blocks, then a prefix count over block order assigns pool slots -- the
+//            paper's sequential dense / sparse counters, computed in parallel.
+//   k_pack   one workgroup per (head, block): copies dense blocks (V transposed to channel-major)
+//            and writes kept values + 2-bit positions of 2:4 blocks.
+// Losses are integer sums of floor(|x| * 2^24), so the result does not depend on summation order
+// and equal inputs give equal bytes.
+#include "hs_device.h"
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+constexpr int kD = 128;  // head_dim handled on the GPU
+
+// ----------------------------------------------------------------------------------------------
+// k_score
+
+__device__ __forceinline__ void score_group(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                            uint64_t &drop, uint64_t &all) {
+  uint32_t a0 = x0 & 0x7FFFu, a1 = x1 & 0x7FFFu, a2 = x2 & 0x7FFFu, a3 = x3 & 0x7FFFu;
+  uint64_t f0 = fixed_mag(a0), f1 = fixed_mag(a1), f2 = fixed_mag(a2), f3 = fixed_mag(a3);
+  uint32_t keep = keep_mask(a0, a1, a2, a3);
+  all += f0 + f1 + f2 + f3;
+  drop += ((keep & 1u) ? 0ull : f0) + ((keep & 2u) ? 0ull : f1) + ((keep & 4u) ? 0ull : f2) +
+          ((keep & 8u) ? 0ull : f3);
+}
+
+__device__ __forceinline__ uint32_t elem(const uint4 &v, int e) {
+  uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
+  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
+                                               const uint16_t *__restrict__ V,
+                                               uint64_t *__restrict__ keys, int L) {
+  const int i = blockIdx.x, nb = gridDim.x, tid = threadIdx.x;
+  const size_t base = (size_t)blockIdx.y * L * kD + (size_t)i * B * kD;
+  const uint16_t *Kb = K + base, *Vb = V + base;
+  uint64_t kk = 0, kv = 0, kp = 0;
+  const int c8 = tid & 15;  // eight consecutive channels
+#pragma unroll
+  for (int g = tid >> 4; g < B / 4; g += 16) {  // four consecutive tokens
+    uint4 kr[4], vr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kr[r] = *reinterpret_cast<const uint4 *>(Kb + (size_t)(4 * g + r) * kD + 8 * c8);
+      vr[r] = *reinterpret_cast<const uint4 *>(Vb + (size_t)(4 * g + r) * kD + 8 * c8);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // K: groups of four channels of one token
+      score_group(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk, kp);
+      score_group(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk, kp);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)  // V: groups of four tokens of one channel
+      score_group(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kk += shfl_xor_u64(kk, m);
+    kv += shfl_xor_u64(kv, m);
+    kp += shfl_xor_u64(kp, m);
+  }
+  __shared__ uint64_t part[4][3];
+  if ((tid & 63) == 0) {
+    part[tid >> 6][0] = kk;
+    part[tid >> 6][1] = kv;
+    part[tid >> 6][2] = kp;
+  }
+  __syncthreads();
+  if (tid < 3) {
+    uint64_t s = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    keys[((size_t)blockIdx.y * nb + i) * 3 + tid] = s;
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
+// k_rank
+
+constexpr int kRankThreads = 1024;
+
+// Ascending bitonic sort of (key, idx) pairs of length n (a power of two) in LDS.
+__device__ void bitonic_sort(uint64_t *key, uint16_t *idx, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < n / 2; t += kRankThreads) {
+        int a = (t / j) * 2 * j + (t % j), b = a + j;
+        bool up = (a & k) == 0;
+        uint64_t ka = key[a], kb = key[b];
+        uint16_t ia = idx[a], ib = idx[b];
+        bool a_gt_b = ka > kb || (ka == kb && ia > ib);
+        if (a_gt_b == up) {
+          key[a] = kb;
+          key[b] = ka;
+          idx[a] = ib;
+          idx[b] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restrict__ keys, int nb,
+                                                       int n_p, int n_sk, int n_sv,
+                                                       int32_t *__restrict__ map_k,
+                                                       int32_t *__restrict__ map_v) {
+  __shared__ uint64_t skey[kMaxBlocks];
+  __shared__ uint16_t sidx[kMaxBlocks];
+  __shared__ uint8_t mode[2][kMaxBlocks];  // 0 pruned, 1 dense, 2 2:4
+  __shared__ int scan[2][kRankThreads];
+  const int hd = blockIdx.x, tid = threadIdx.x;
+  const uint64_t *hk = keys + (size_t)hd * nb * 3;
+  int n = 2;
+  while (n < nb) n <<= 1;
+
+  // Pruned blocks: the n_p smallest whole-block magnitudes.
+  for (int t = tid; t < n; t += kRankThreads) {
+    skey[t] = t < nb ? hk[3 * t + 2] : ~0ull;
+    sidx[t] = (uint16_t)t;
+  }
+  __syncthreads();
+  bitonic_sort(skey, sidx, n);
+  for (int t = tid; t < nb; t += kRankThreads) {
+    uint8_t m = t < n_p ? 0 : 1;
+    mode[0][sidx[t]] = m;
+    mode[1][sidx[t]] = m;
+  }
+  __syncthreads();
+
+  // Eq. (2d) per tensor among the survivors: the n_s smallest 2:4 losses become 2:4. Pruned
+  // blocks carry the largest key, which no real loss reaches (|x| < 2^24 keeps losses < 2^63).
+  for (int x = 0; x < 2; ++x) {
+    const int want = x ? n_sv : n_sk;
+    for (int t = tid; t < n; t += kRankThreads) {
+      skey[t] = (t < nb && mode[x][t] != 0) ? hk[3 * t + x] : ~0ull;
+      sidx[t] = (uint16_t)t;
+    }
+    __syncthreads();
+    bitonic_sort(skey, sidx, n);
+    for (int t = tid; t < want; t += kRankThreads) mode[x][sidx[t]] = 2;
+    __syncthreads();
+  }
+
+  // Pool slots in block order: exclusive prefix counts of dense and 2:4 blocks.
+  constexpr int kPer = kMaxBlocks / kRankThreads;
+  for (int x = 0; x < 2; ++x) {
+    const int ns = x ? n_sv : n_sk, nd = nb - n_p - ns;
+    int cd = 0, cs = 0;
+    for (int e = 0; e < kPer; ++e) {
+      int i = tid * kPer + e;
+      if (i < nb) {
+        cd += mode[x][i] == 1;
+        cs += mode[x][i] == 2;
+      }
+    }
+    scan[0][tid] = cd;
+    scan[1][tid] = cs;
+    __syncthreads();
+    for (int off = 1; off < kRankThreads; off <<= 1) {
+      int vd = tid >= off ? scan[0][tid - off] : 0, vs = tid >= off ? scan[1][tid - off] : 0;
+      __syncthreads();
+      scan[0][tid] += vd;
+      scan[1][tid] += vs;
+      __syncthreads();
+    }
+    int rd = scan[0][tid] - cd + hd * nd, rs = scan[1][tid] - cs + hd * ns;
+    int32_t *map = (x ? map_v : map_k) + (size_t)hd * nb;
+    for (int e = 0; e < kPer; ++e) {
+      int i = tid * kPer + e;
+      if (i < nb) {
+        uint8_t m = mode[x][i];
+        map[i] = m == 0 ? 0 : (m == 1 ? ++rd : -(++rs));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
+// k_pack
+
+template <int B>
+__global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ K,
+                                              const uint16_t *__restrict__ V,
+                                              const int32_t *__restrict__ map_k,
+                                              const int32_t *__restrict__ map_v, CacheView c,
+                                              int L) {
+  constexpr int BD = B * kD;
+  const int i = blockIdx.x, nb = gridDim.x, tid = threadIdx.x;
+  const size_t base = (size_t)blockIdx.y * L * kD + (size_t)i * BD;
+  const int32_t mk = map_k[(size_t)blockIdx.y * nb + i], mv = map_v[(size_t)blockIdx.y * nb + i];
+
+  // K: dense copy, or per token: four groups of four channels -> 8 kept values + 1 meta word.
+  if (mk > 0) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(K + base);
+    uint4 *dst = reinterpret_cast<uint4 *>(c.k_dense + (size_t)(mk - 1) * BD);
+#pragma unroll
+    for (int e = tid; e < BD / 8; e += 256) dst[e] = src[e];
+  } else if (mk < 0) {
+    const size_t s = (size_t)(-mk - 1);
+    uint16_t *nnz = c.k_nnz + s * (BD / 2), *meta = c.k_meta + s * (BD / 16);
+#pragma unroll
+    for (int item = tid; item < B * (kD / 16); item += 256) {
+      const int t = item >> 3, w = item & 7;
+      const uint4 *p = reinterpret_cast<const uint4 *>(K + base + (size_t)t * kD + 16 * w);
+      const uint4 x0 = p[0], x1 = p[1];
+      const uint32_t wd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t pairs[4], word = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t e0 = wd[2 * g] & 0xFFFFu, e1 = wd[2 * g] >> 16;
+        uint32_t e2 = wd[2 * g + 1] & 0xFFFFu, e3 = wd[2 * g + 1] >> 16;
+        uint32_t nib = mask_to_nibble(
+            keep_mask(e0 & 0x7FFFu, e1 & 0x7FFFu, e2 & 0x7FFFu, e3 & 0x7FFFu));
+        pairs[g] = kept_pair(nib, e0, e1, e2, e3);
+        word |= nib << (4 * g);
+      }
+      *reinterpret_cast<uint4 *>(nnz + (size_t)t * (kD / 2) + 8 * w) =
+          make_uint4(pairs[0], pairs[1], pairs[2], pairs[3]);
+      meta[(size_t)t * (kD / 16) + w] = (uint16_t)word;
+    }
+  }
+
+  // V: work item = (four consecutive tokens g, eight consecutive channels c8); the lanes holding
+  // the four token groups of one metadata word are lane, lane^16, lane^32, lane^48.
+  if (mv != 0) {
+    const bool dense = mv > 0;
+    const size_t s = dense ? (size_t)(mv - 1) : (size_t)(-mv - 1);
+#pragma unroll
+    for (int item = tid; item < (B / 4) * 16; item += 256) {
+      const int g = item >> 4, c8 = item & 15;
+      uint4 vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vr[r] = *reinterpret_cast<const uint4 *>(V + base + (size_t)(4 * g + r) * kD + 8 * c8);
+      if (dense) {
+        uint16_t *dst = c.v_dense + s * BD;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint2 out = make_uint2(elem(vr[0], e) | (elem(vr[1], e) << 16),
+                                 elem(vr[2], e) | (elem(vr[3], e) << 16));
+          *reinterpret_cast<uint2 *>(dst + (size_t)(8 * c8 + e) * B + 4 * g) = out;
+        }
+      } else {
+        uint16_t *nnz = c.v_nnz + s * (BD / 2), *meta = c.v_meta + s * (BD / 16);
+        uint32_t words[4] = {0, 0, 0, 0};  // metadata words of channels 8*c8 + e, two per dword
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t x0 = elem(vr[0], e), x1 = elem(vr[1], e), x2 = elem(vr[2], e),
+                   x3 = elem(vr[3], e);
+          uint32_t nib = mask_to_nibble(
+              keep_mask(x0 & 0x7FFFu, x1 & 0x7FFFu, x2 & 0x7FFFu, x3 & 0x7FFFu));
+          *reinterpret_cast<uint32_t *>(nnz + (size_t)(8 * c8 + e) * (B / 2) + 2 * g) =
+              kept_pair(nib, x0, x1, x2, x3);
+          words[e >> 1] |= nib << (4 * (g & 3) + 16 * (e & 1));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          words[q] |= __shfl_xor(words[q], 16, 64);
+          words[q] |= __shfl_xor(words[q], 32, 64);
+        }
+        // lane group g & 3 == q stores the words of channels 8*c8 + 2q, 8*c8 + 2q + 1
+        const int q = g & 3;
+        const uint32_t wq = q == 0 ? words[0] : (q == 1 ? words[1] : (q == 2 ? words[2] : words[3]));
+        meta[(size_t)(8 * c8 + 2 * q) * (B / 16) + (g >> 2)] = (uint16_t)(wq & 0xFFFFu);
+        meta[(size_t)(8 * c8 + 2 * q + 1) * (B / 16) + (g >> 2)] = (uint16_t)(wq >> 16);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
+                           uint64_t *keys, hipStream_t stream) {
+  const dim3 grid(d.nb, d.b * d.hkv);
+  if (d.B == 64)
+    k_score<64><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+  else
+    k_score<128><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_rank<<<d.b * d.hkv, kRankThreads, 0, stream>>>(keys, d.nb, d.np, d.nsk, d.nsv, c.map_k,
+                                                   c.map_v);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d.B == 64)
+    k_pack<64><<<grid, 256, 0, stream>>>(k, v, c.map_k, c.map_v, c, d.L);
+  else
+    k_pack<128><<<grid, 256, 0, stream>>>(k, v, c.map_k, c.map_v, c, d.L);
+  return hipGetLastError();
+}
+
+}  // namespace hs

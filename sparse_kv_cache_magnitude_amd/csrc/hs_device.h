@@ -1,0 +1,136 @@
+// hs_device.h -- device-side building blocks shared by the gfx950 kernels of libhierasparse.
+//
+// Operand layouts of the matrix-core instructions used below (wave64, one 16x16 output tile,
+// "chunk" = l / 16 for lane l):
+//   v_mfma_f32_16x16x32_bf16   A[16][32] x B[32][16]: lane l holds row (A) / column (B) l % 16
+//                              and k = 8*chunk .. 8*chunk + 7.
+//   v_smfmac_f32_16x16x64_bf16 A is 2:4 along k. Lane l holds 8 kept values of row l % 16 for
+//                              the logical k = 16*chunk .. 16*chunk + 15 (four groups of four);
+//                              value e sits at position bits [2e+1:2e] of the low 16 index bits
+//                              (abid 0) inside group e / 2. B lane l holds column l % 16 at
+//                              k = 8*chunk + s for slots s = 0..7 and 32 + 8*chunk + (s - 8) for
+//                              slots 8..15, i.e. two 16x16x32 B operands back to back.
+//   accumulator                lane l holds rows 4*chunk .. 4*chunk + 3 of column l % 16.
+// These were checked on gfx950 hardware against a CPU product of random integer-valued operands.
+// Consequences used by the kernels:
+//   * the index word of one lane is exactly one 16-bit metadata word of the packed format
+//     (four groups, first kept position in the low two bits of each nibble);
+//   * the B registers of a 64-deep SMFMAC are the B registers of two consecutive 32-deep dense
+//     MFMAs, so dense and 2:4 tiles share the same query (GEMM1) and probability (GEMM2) registers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x16 as_bf16x16(uint4 lo, uint4 hi) {
+  struct P {
+    uint4 a, b;
+  } p{lo, hi};
+  return __builtin_bit_cast(bf16x16, p);
+}
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// 2:4 sparse A (8 kept bf16 of 16 logical k) times dense B (two 16x16x32 B operands).
+__device__ __forceinline__ f32x4 smfmac16(uint4 a, uint4 b_lo, uint4 b_hi, uint32_t idx,
+                                          f32x4 c) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b_lo, b_hi), c,
+                                                    (int)idx, 0, 0);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even, gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ----------------------------------------------------------------------------------------------
+// Magnitude pruning of one group of four bf16 values.
+
+// floor(|x| * 2^24) of a bf16 magnitude (bits & 0x7FFF), |x| < 2^24. A normal bf16 is
+// (128 + m) * 2^(e - 134); scaled by 2^24 that is (128 + m) shifted by e - 110.
+__device__ __forceinline__ uint64_t fixed_mag(uint32_t a) {
+  int s = (int)(a >> 7) - 110;
+  uint32_t man = (a & 0x7Fu) | 0x80u;
+  uint64_t up = (uint64_t)man << (s > 0 ? s : 0);
+  uint32_t down = (s > -8) ? (man >> (s < 0 ? -s : 0)) : 0u;
+  return s >= 0 ? up : (uint64_t)down;
+}
+
+// Keep the two largest magnitudes of (a0..a3); equal magnitudes keep the lower position.
+// Returns the 4-bit kept mask; element j is kept when fewer than two others beat it, where k
+// beats j if a_k > a_j, or a_k == a_j and k < j.
+__device__ __forceinline__ uint32_t keep_mask(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  uint32_t b01 = a0 >= a1, b02 = a0 >= a2, b03 = a0 >= a3;
+  uint32_t b12 = a1 >= a2, b13 = a1 >= a3, b23 = a2 >= a3;
+  uint32_t r0 = 3u - b01 - b02 - b03;
+  uint32_t r1 = b01 + 2u - b12 - b13;
+  uint32_t r2 = b02 + b12 + 1u - b23;
+  uint32_t r3 = b03 + b13 + b23;
+  return (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) |
+         ((uint32_t)(r3 < 2) << 3);
+}
+
+// Kept mask -> metadata nibble (first position in bits 1:0, second in bits 3:2). The six valid
+// masks 0b0011, 0b0101, 0b0110, 0b1001, 0b1010, 0b1100 map to 0x4, 0x8, 0x9, 0xC, 0xD, 0xE.
+__device__ __forceinline__ uint32_t mask_to_nibble(uint32_t mask) {
+  constexpr uint64_t kTable = (0x4ull << 12) | (0x8ull << 20) | (0x9ull << 24) | (0xCull << 36) |
+                              (0xDull << 40) | (0xEull << 48);
+  return (uint32_t)(kTable >> (4 * mask)) & 0xFu;
+}
+
+// Pack the two kept values of a group (x0..x3 as bf16 bits) into one dword, first kept in the
+// low half.
+__device__ __forceinline__ uint32_t kept_pair(uint32_t nib, uint32_t x0, uint32_t x1, uint32_t x2,
+                                              uint32_t x3) {
+  uint32_t i0 = nib & 3u, i1 = nib >> 2;
+  uint32_t v0 = i0 == 0 ? x0 : (i0 == 1 ? x1 : x2);
+  uint32_t v1 = i1 == 1 ? x1 : (i1 == 2 ? x2 : x3);
+  return v0 | (v1 << 16);
+}
+
+// Expand one packed group (pair = first | second << 16, nibble) back to its four slots, as two
+// dwords (slots 0,1 and slots 2,3) with zeros in the dropped slots.
+__device__ __forceinline__ uint2 expand_group(uint32_t pair, uint32_t nib) {
+  uint32_t i0 = nib & 3u, i1 = nib >> 2;
+  uint32_t lo = pair & 0xFFFFu, hi = pair >> 16;
+  uint32_t s0 = (i0 == 0 ? lo : 0u);
+  uint32_t s1 = (i0 == 1 ? lo : 0u) | (i1 == 1 ? hi : 0u);
+  uint32_t s2 = (i0 == 2 ? lo : 0u) | (i1 == 2 ? hi : 0u);
+  uint32_t s3 = (i1 == 3 ? hi : 0u);
+  return make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
+}
+
+// ----------------------------------------------------------------------------------------------
+// Token order inside a 64-token tile.
+//
+// GEMM1 (S^T = K Q^T) produces four 16-row accumulator tiles; lane chunk g of tile t holds rows
+// 4g..4g+3. GEMM2 (O^T = V^T P^T) wants, in lane chunk g, the probabilities of tokens
+// 8g..8g+7 (B slots 0..7) and 32+8g..32+8g+7 (B slots 8..15). Feeding GEMM1 row r of tile t with
+// token tile_token(t, r) makes the accumulators land exactly there, so P^T needs no data movement
+// between lanes: each lane only packs its own fp32 values to bf16.
+__device__ __forceinline__ int tile_token(int t, int r) {
+  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+
+// ----------------------------------------------------------------------------------------------
+// Wave helpers.
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = __shfl_xor((uint32_t)v, mask, 64), hi = __shfl_xor((uint32_t)(v >> 32), mask, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace hs

@@ -1,0 +1,34 @@
+// hs_internal.h -- host-side launch interface between the C ABI (hs_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+constexpr int kMaxBlocks = 4096;  // blocks per head handled by the in-LDS ranking
+
+// Validated problem description (see hs_api.hip).
+struct Dims {
+  int b, hq, hkv, G;  // batch, query heads, KV heads, query heads per KV head
+  int L, D, B, nb;    // tokens, head_dim, block size, blocks per head
+  int np, nsk, nsv;   // per-head pruned / K 2:4 / V 2:4 block counts
+  int ndk, ndv;       // per-head dense block counts
+};
+
+struct CacheView {
+  int32_t *map_k, *map_v;
+  uint16_t *k_dense, *k_nnz, *k_meta;
+  uint16_t *v_dense, *v_nnz, *v_meta;
+};
+
+hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
+                           uint64_t *keys, hipStream_t stream);
+
+hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
+                         float *lse, float scale_log2, int splits, float *part_o, float *part_lse,
+                         hipStream_t stream);
+
+hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
+                          float *lse, float scale_log2, bool smfmac, hipStream_t stream);
+
+}  // namespace hs

@@ -1,0 +1,80 @@
+"""GPU compressor (hs_compress) against the oracle: maps and all six pools bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Dims
+from sparse_kv_cache_magnitude_amd import hierasparse as hs
+from sparse_kv_cache_magnitude_amd import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(b, hkv, L, B, counts, K, V, hq=None):
+    hq = hq or hkv
+    shp = hs.shape(b, hq, hkv, L, 128, B)
+    cnt = hs.counts(*counts)
+    print(f"[compress] b={b} hkv={hkv} L={L} B={B} counts={counts}", flush=True)
+    cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+    want = oracle.compress(Dims(b, hkv, L, 128, B, *counts), K, V)
+    gu.compare_cache(gu.cache_to_numpy(cache), want)
+    return cache
+
+
+@pytest.mark.parametrize("name", ["decode_1h_4k_all24", "prefill_16k_b1_B128",
+                                  "decode_llama8b_32k_b8", "decode_128k_b4"])
+def test_compress_workloads_bit_exact(name):
+    w = synth.workload(name)
+    K, V = gu.workload_kv(name)
+    _check(w.b, w.hkv, w.L, w.B, w.counts(), K, V, hq=w.hq)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("counts_fn", [
+    lambda nb: (0, 0, 0),            # all dense
+    lambda nb: (0, nb, nb),          # all 2:4
+    lambda nb: (nb, 0, 0),           # all pruned
+    lambda nb: (1, nb - 1, 0),       # K all sparse, V all dense among survivors
+    lambda nb: (nb // 3, nb // 2, nb // 5),
+])
+def test_compress_edge_counts(B, counts_fn):
+    rng = np.random.default_rng(B)
+    b, hkv, L = 3, 2, 9 * B   # nb = 9: not a power of two
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32) * 3)
+    _check(b, hkv, L, B, counts_fn(L // B), K, V)
+
+
+def test_compress_single_block_and_ties():
+    rng = np.random.default_rng(7)
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 2.0, 0.5, -2.0], np.float32)
+    b, hkv, L, B = 2, 3, 64 * 6, 64
+    K = synth.bf16_bits(vals[rng.integers(0, len(vals), (b, hkv, L, 128))])
+    V = synth.bf16_bits(vals[rng.integers(0, len(vals), (b, hkv, L, 128))])
+    K[:, :, 64:128] = K[:, :, 256:320]     # duplicated blocks -> tied block losses
+    V[:, :, 64:128] = V[:, :, 256:320]
+    _check(b, hkv, L, B, (2, 2, 3), K, V)
+    _check(1, 1, 64, 64, (0, 1, 0), K[:1, :1, :64], V[:1, :1, :64])   # nb = 1
+
+
+def test_compress_extreme_magnitudes():
+    rng = np.random.default_rng(11)
+    b, hkv, L, B = 1, 2, 512, 64
+    mag = np.exp2(rng.integers(-130, 24, (b, hkv, L, 128))).astype(np.float32)
+    sign = np.where(rng.random((b, hkv, L, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    K = synth.bf16_bits(mag * sign * rng.uniform(1, 1.99, (b, hkv, L, 128)).astype(np.float32))
+    V = synth.bf16_bits(np.flip(mag, axis=2) * sign)
+    K = np.where(np.abs(synth.bf16_to_f32(K)) >= 2.0 ** 24, 0, K).astype(np.uint16)
+    _check(b, hkv, L, B, (2, 3, 3), K, V)
+
+
+def test_compress_deterministic():
+    w = synth.workload("decode_1h_4k_all24")
+    K, V = gu.workload_kv(w.name)
+    shp, cnt = hs.shape(1, 1, 1, w.L, 128, w.B), hs.counts(0, 40, 20)
+    Kd, Vd = gu.to_dev(K), gu.to_dev(V)
+    a = gu.cache_to_numpy(gu.gpu_compress(shp, cnt, Kd, Vd))
+    b = gu.cache_to_numpy(gu.gpu_compress(shp, cnt, Kd, Vd))
+    gu.compare_cache(a, b)
