@@ -16,12 +16,22 @@ pytestmark = pytest.mark.gpu
 MAX_ABS, REL_L2 = 1e-2, 5e-3
 
 
+def half_ulp_bf16(x):
+    """Half a bf16 ulp at |x|: the error of rounding an exact result to the bf16 output."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
 def assert_close(o_gpu, o_ref, lse_gpu=None, lse_ref=None, tag=""):
+    """max |o - o_ref| <= 1e-2 per element, plus the final rounding of the output to bf16 (half an
+    ulp of o_ref; it alone exceeds 1e-2 once |o| >= 4), and relative L2 <= 5e-3 overall."""
     o_gpu = np.asarray(o_gpu, np.float64).reshape(o_ref.shape)
     err = np.abs(o_gpu - o_ref)
     rel = np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-30)
-    print(f"[{tag}] max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
-    assert err.max() <= MAX_ABS and rel <= REL_L2, (err.max(), rel)
+    excess = (err - half_ulp_bf16(o_ref)).max()
+    print(f"[{tag}] max_abs={err.max():.3e} max_abs_beyond_output_rounding={excess:.3e} "
+          f"rel_l2={rel:.3e}", flush=True)
+    assert excess <= MAX_ABS and rel <= REL_L2, (err.max(), excess, rel)
     if lse_gpu is not None:
         lg = np.asarray(lse_gpu, np.float64).reshape(lse_ref.shape)
         fin = np.isfinite(lse_ref)

@@ -1,0 +1,138 @@
+"""GPU causal prefill (hs_prefill_attn) against the oracle's fp64 causal attention over the
+decompressed cache, for both ways 2:4 tiles reach the matrix cores (SMFMAC and decompress-to-LDS).
+Gate: max |o - o_ref| <= 1e-2 and relative L2 <= 5e-3 (sampled query rows at full size)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Dims
+from sparse_kv_cache_magnitude_amd import hierasparse as hs
+from sparse_kv_cache_magnitude_amd import synth
+from tests import gpu_util as gu
+from tests.test_gpu_decode import assert_close
+
+pytestmark = pytest.mark.gpu
+
+FLAGS = {"smfmac": hs.HS_PREFILL_SMFMAC, "decompress": hs.HS_PREFILL_DECOMPRESS}
+
+
+def run_prefill(b, hq, hkv, L, B, counts, K, V, Q, flags, scale=0.0, cache=None):
+    shp = hs.shape(b, hq, hkv, L, 128, B)
+    cnt = hs.counts(*counts)
+    if cache is None:
+        cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+    qd = gu.to_dev(Q)
+    o = torch.empty((b, hq, L, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b, hq, L), dtype=torch.float32, device="cuda")
+    hs.hs_prefill_attn(shp, cnt, cache, qd, o, lse, scale, flags)
+    torch.cuda.synchronize()
+    return synth.bf16_to_f32(gu.to_host_u16(o)), lse.cpu().numpy(), cache
+
+
+def sample_rows(b, hq, L, per_head, seed):
+    """Flat row ids into [b][hq][L]: per head the first and last rows, rows around every 64-token
+    tile edge of a few tiles, plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for bi in range(b):
+        for h in range(hq):
+            base = (bi * hq + h) * L
+            pick = {0, 1, 63, 64, 65, L - 1, L - 64}
+            pick.update(rng.integers(0, L, per_head).tolist())
+            rows += [base + r for r in sorted(pick) if 0 <= r < L]
+    return np.array(rows, np.int64)
+
+
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+@pytest.mark.parametrize("B,counts", [(64, (0, 0, 0)), (64, (3, 9, 5)), (64, (0, 16, 16)),
+                                      (128, (1, 5, 2)), (128, (0, 0, 8))])
+def test_prefill_small_full_compare(path, B, counts):
+    rng = np.random.default_rng(B + sum(counts))
+    b, hq, hkv, L = 2, 8, 2, 16 * 64 if B == 64 else 8 * 128
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    print(f"[prefill] {path} B={B} counts={counts}", flush=True)
+    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
+    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q)
+    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} B={B} {counts}")
+
+
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_prefill_gqa_groups(path, G):
+    rng = np.random.default_rng(100 + G)
+    b, hkv, L, B = 1, 2, 5 * 64, 64
+    hq = G * hkv
+    counts = (1, 2, 2)
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path], scale=0.07)
+    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q,
+                                  0.07)
+    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} G={G}")
+
+
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+def test_prefill_pruned_prefix_rows_are_empty(path):
+    """Rows whose visible set is empty (their own and all earlier blocks pruned) give 0 / -inf."""
+    rng = np.random.default_rng(3)
+    b, hq, hkv, L, B = 1, 4, 1, 4 * 64, 64
+    scale = np.ones((1, 1, L, 1), np.float32)
+    scale[:, :, :128] = 1e-3   # blocks 0 and 1 have the smallest magnitude -> pruned
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32) * scale)
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32) * scale)
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    counts = (2, 1, 1)
+    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
+    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q)
+    assert np.isneginf(ref_lse).any()   # the data makes the first blocks' rows empty
+    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} empty rows")
+
+
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+def test_prefill_workload_sampled(path):
+    """Full-size causal prefill (16K tokens, 32/8 heads, 128-token blocks, 70% 2:4) on sampled
+    rows, in the launch configuration the benchmark times."""
+    w = synth.workload("prefill_16k_b1_B128")
+    K, V = gu.workload_kv(w.name)
+    Q = synth.make_q(w.seed, w.b, w.hq, w.L, w.D)
+    print(f"[prefill] {w.name} {path}", flush=True)
+    o, lse, cache = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q, FLAGS[path])
+    rows = sample_rows(w.b, w.hq, w.L, 6, 7)
+    ref, ref_lse = oracle.prefill(Dims(w.b, w.hkv, w.L, 128, w.B, *w.counts()),
+                                  gu.cache_to_numpy(cache), Q, rows=rows)
+    assert_close(o.reshape(-1, 128)[rows], ref, lse.reshape(-1)[rows], ref_lse,
+                 f"{w.name} {path}")
+
+
+def test_prefill_paths_agree_and_deterministic():
+    rng = np.random.default_rng(21)
+    b, hq, hkv, L, B = 1, 8, 2, 1024, 64
+    counts = (2, 6, 9)
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    o1, l1, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_SMFMAC)
+    o1b, l1b, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_SMFMAC, cache=cache)
+    o2, l2, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_DECOMPRESS,
+                            cache=cache)
+    assert np.array_equal(o1, o1b) and np.array_equal(l1, l1b)
+    # the two paths multiply the same bf16 values; only accumulation order may differ
+    assert np.abs(o1 - o2).max() <= 1e-2
+
+
+def test_prefill_dense_equals_library_attention():
+    rng = np.random.default_rng(22)
+    b, hq, hkv, L, B = 1, 4, 1, 512, 64
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    o, _, _ = run_prefill(b, hq, hkv, L, B, (0, 0, 0), K, V, Q, hs.HS_PREFILL_SMFMAC)
+    qt = torch.from_numpy(synth.bf16_to_f32(Q))
+    kt = torch.from_numpy(synth.bf16_to_f32(K)).repeat_interleave(hq // hkv, dim=1)
+    vt = torch.from_numpy(synth.bf16_to_f32(V)).repeat_interleave(hq // hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).numpy()
+    assert_close(o, ref.astype(np.float64), tag="prefill dense vs sdpa fp32")
