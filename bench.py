@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the hierarchical sparse KV attention hot path on one MI355X.
+
+One step = the whole hot path over one batch of the Llama-3.1-8B attention workload (32 query /
+8 KV heads, head_dim 128, 32K context, batch 8, 64-token blocks, 25% dense / 60% 2:4 / 15% pruned
+blocks -- the batch-8, 32K kernel benchmark setting of HieraSparse v2 §V-B1):
+  hs_compress (score, rank, pack) of the 32K-token K/V cache,
+  hs_prefill_attn causal over the 32K prompt (2:4 blocks on SMFMAC),
+  hs_decode_attn of one new token per query head over the compressed cache.
+Each call is bracketed by HIP events on the stream the kernels run on. The same kernels on a cache
+compressed with every block dense give the same-kernel dense baseline.
+
+Output: one JSON line. value = decode HBM throughput (GB/s) on the compressed bytes the decode
+must read; roofline = the step's dominant kernel (prefill, matrix cores); the other kernels'
+rooflines, times and speedups vs dense are extra keys. The CPU oracle is timed on a bounded sample
+of the same workload on the host cores (cpu_baseline).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "decode_llama8b_32k_b8"
+HBM_PEAK_GBS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--prefill-path", choices=["smfmac", "decompress"], default="smfmac")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense-baseline", action="store_true")
+    p.add_argument("--cpu-sample-heads", type=int, default=16,
+                   help="(batch, KV head) pairs the oracle runs for the CPU baseline")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# Algorithmic work (bytes and flops the method must move / execute), from the mode table.
+
+def decode_bytes(w, G):
+    """Compressed K/V blocks the decode must stream, both index maps, q in and o out."""
+    B, D, nb = w.B, w.D, w.nb
+    ndk, ndv = nb - w.n_p - w.n_sk, nb - w.n_p - w.n_sv
+    per_head = (ndk + ndv) * 2 * B * D + (w.n_sk + w.n_sv) * (B * D + B * D // 8) \
+        + 2 * 4 * nb + 2 * G * D * 2
+    return per_head * w.b * w.hkv
+
+
+def compress_bytes(w, cache_bytes):
+    """Two passes over K and V (score, pack) plus the compressed output."""
+    return 2 * 2 * w.b * w.hkv * w.L * w.D * 2 + sum(cache_bytes.values())
+
+
+def prefill_flops(w, map_k, map_v, smfmac=True):
+    """Causal attention work over visible (query, key) pairs with key <= query: dense-equivalent
+    flops (4*D per pair) and the flops the matrix cores must execute, where a 2:4 operand costs
+    half (Eq. 9 of HieraSparse v2 §III-D2) on the SMFMAC path and full on the decompress path."""
+    import numpy as np
+    B, D, L = w.B, w.D, w.L
+    nb = L // B
+    i = np.arange(nb, dtype=np.float64)
+    # pairs (q, k) with k in block i and q >= k: sum over the block's tokens of (L - k)
+    pairs = B * L - B * i * B - B * (B - 1) / 2.0
+    mk = np.asarray(map_k).reshape(-1, nb)
+    mv = np.asarray(map_v).reshape(-1, nb)
+    vis = mk != 0
+    ck = np.where(mk > 0, 1.0, 0.5 if smfmac else 1.0)
+    cv = np.where(mv > 0, 1.0, 0.5 if smfmac else 1.0)
+    G = w.hq // w.hkv
+    dense_eq = float((vis * pairs).sum()) * 4 * D * G
+    executed = float((vis * pairs * (ck + cv)).sum()) * 2 * D * G
+    full_causal = 4 * D * L * (L + 1) / 2 * w.hq * w.b
+    return dense_eq, executed, full_causal
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_kv_cache_magnitude_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------
+
+def make_inputs(w, torch, dev):
+    """Seeded N(0,1) bf16 K, V, prompt Q and decode q of the workload shape, drawn on the device
+    (torch's seeded generator; the timing does not depend on the values), with the workload's
+    key outlier channels scaled by 8."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    K = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
+    K = K.to(torch.bfloat16)
+    if w.outliers:
+        for h in range(w.hkv):
+            ch = torch.randperm(w.D, generator=g, device=dev)[:w.outliers]
+            K[:, h, :, ch] *= 8
+    V = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev,
+                    dtype=torch.float32).to(torch.bfloat16)
+    Q = torch.empty((w.b, w.hq, w.L, w.D), device=dev, dtype=torch.bfloat16)
+    for bi in range(w.b):
+        Q[bi] = torch.randn((w.hq, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
+    q = torch.randn((w.b, w.hq, w.D), generator=g, device=dev, dtype=torch.float32)
+    return K, V, Q, q.to(torch.bfloat16)
+
+
+def cpu_baseline(w, heads, min_seconds=10.0):
+    """The oracle (C, fp64, OpenMP) on `heads` (batch, KV head) pairs of the workload: compress
+    their K/V, then decode their query heads over the result. Reported in the metric's unit: GB/s
+    of compressed decode bytes, i.e. decode_bytes of the sample / oracle decode time."""
+    import numpy as np
+    import oracle
+    from oracle import Dims
+    from sparse_kv_cache_magnitude_amd import synth
+    G = w.hq // w.hkv
+    K, V = synth.make_kv(w.seed, 1, heads, w.L, w.D, outliers=w.outliers)
+    q = synth.make_q(w.seed, 1, heads * G, 1, w.D)
+    d = Dims(1, heads, w.L, w.D, w.B, w.n_p, w.n_sk, w.n_sv)
+    t0 = time.perf_counter()
+    cache = oracle.compress(d, K, V)
+    t1 = time.perf_counter()
+    reps = 0
+    while True:  # repeat the decode for about ten seconds of CPU time
+        oracle.decode(d, cache, q, heads * G)
+        reps += 1
+        t2 = time.perf_counter()
+        if t2 - t1 >= min_seconds:
+            break
+    per = (t2 - t1) / reps
+    sample_w = synth.Workload(**{**w.__dict__, "b": 1, "hkv": heads, "hq": heads * G})
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(decode_bytes(sample_w, G) / per / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.b * w.hkv} (batch, KV head) pairs of {w.name}: fp64 decode "
+                      f"(decompress + attention) of their {heads * G} query heads over "
+                      f"{w.L} tokens, repeated {reps}x; compress of the same heads took "
+                      f"{t1 - t0:.2f} s",
+            "decode_s_per_rep": round(per, 4), "compress_s": round(t1 - t0, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from sparse_kv_cache_magnitude_amd import hierasparse as hs
+    from sparse_kv_cache_magnitude_amd import synth
+
+    w = synth.workload(WORKLOAD)
+    G = w.hq // w.hkv
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    flags = hs.HS_PREFILL_SMFMAC if args.prefill_path == "smfmac" else hs.HS_PREFILL_DECOMPRESS
+
+    K, V, Q, q = make_inputs(w, torch, dev)
+    shp = hs.shape(w.b, w.hq, w.hkv, w.L, w.D, w.B)
+    cnt = hs.counts(w.n_p, w.n_sk, w.n_sv)
+    cache = hs.alloc_cache(shp, cnt)
+    ws_c = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+    ws_d = hs.alloc_workspace(hs.HS_OP_DECODE, shp, cnt)
+    O = torch.empty_like(Q)
+    lse_p = torch.empty((w.b, w.hq, w.L), device=dev, dtype=torch.float32)
+    o = torch.empty_like(q)
+    lse_d = torch.empty((w.b, w.hq), device=dev, dtype=torch.float32)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        hs.hs_compress(shp, cnt, K, V, cache, ws_c)
+        if ev:
+            ev[1].record(stream)
+        hs.hs_prefill_attn(shp, cnt, cache, Q, O, lse_p, 0.0, flags)
+        if ev:
+            ev[2].record(stream)
+        hs.hs_decode_attn(shp, cnt, cache, q, o, lse_d, 0.0, 0, ws_d)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    comp_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    pre_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+
+    cache_bytes = hs.hs_cache_sizes(shp, cnt)
+    map_k = cache["map_k"].cpu().numpy()
+    map_v = cache["map_v"].cpu().numpy()
+    d_bytes = decode_bytes(w, G)
+    dense_eq, executed, full_causal = prefill_flops(w, map_k, map_v, flags == hs.HS_PREFILL_SMFMAC)
+    c_bytes = compress_bytes(w, cache_bytes)
+
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    pre_s = float(np.mean(pre_ms)) / 1e3
+    comp_s = float(np.mean(comp_ms)) / 1e3
+    decode_gbs = d_bytes / dec_s / 1e9
+    pre_exec_tflops = executed / pre_s / 1e12
+    pre_dense_eq_tflops = dense_eq / pre_s / 1e12
+
+    out = {
+        "metric": "decode attn µs & HBM GB/s at 32K ctx; prefill attn TFLOP/s; speedup vs dense",
+        "value": round(decode_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 3),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 K/V/Q (4 key channels per KV head x8), no weights",
+        "config": {"workload": WORKLOAD, "batch": w.b, "seq_len": w.L, "q_heads": w.hq,
+                   "kv_heads": w.hkv, "head_dim": w.D, "block": w.B,
+                   "blocks_per_head_dense_2to4_pruned": [w.nb - w.n_p - w.n_sk, w.n_sk, w.n_p],
+                   "prefill_2to4_path": args.prefill_path},
+        "decode_us": round(dec_s * 1e6, 2),
+        "decode_bytes": d_bytes,
+        "prefill_ms": round(pre_s * 1e3, 3),
+        "prefill_tflops_dense_equivalent": round(pre_dense_eq_tflops, 1),
+        "prefill_tflops_executed": round(pre_exec_tflops, 1),
+        "prefill_flops": {"dense_equivalent": dense_eq, "executed": executed,
+                          "full_causal_dense": full_causal},
+        "compress_us": round(comp_s * 1e6, 2),
+        "compress_share_of_prefill": round(comp_s / pre_s, 5),
+        "roofline": {"bound": "mfma", "kernel": "k_prefill",
+                     "achieved": round(pre_exec_tflops, 2), "peak": BF16_DENSE_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_exec_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("k_prefill", source_digest(
+                         "hs_prefill.hip", "hs_device.h"))},
+        "roofline_decode": {"bound": "hbm", "kernel": "k_decode_split+k_decode_combine",
+                            "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic("k_decode_split", source_digest(
+                                "hs_decode.hip", "hs_device.h"))},
+        "roofline_compress": {"bound": "hbm", "kernel": "k_score+k_rank+k_pack",
+                              "achieved": round(c_bytes / comp_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s",
+                              "frac": round(c_bytes / comp_s / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+    if not args.no_dense_baseline:
+        # Same kernels, cache compressed with every block dense.
+        cnt0 = hs.counts(0, 0, 0)
+        cache0 = hs.alloc_cache(shp, cnt0)
+        ws_c0 = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt0)
+        ws_d0 = hs.alloc_workspace(hs.HS_OP_DECODE, shp, cnt0)
+        hs.hs_compress(shp, cnt0, K, V, cache0, ws_c0)
+        del ws_c0
+        reps = max(3, args.steps // 2)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for r in range(reps + 1):
+            e = ev[r - 1] if r else None
+            if e:
+                e[0].record(stream)
+            hs.hs_prefill_attn(shp, cnt0, cache0, Q, O, lse_p, 0.0, flags)
+            if e:
+                e[1].record(stream)
+            hs.hs_decode_attn(shp, cnt0, cache0, q, o, lse_d, 0.0, 0, ws_d0)
+            if e:
+                e[2].record(stream)
+        torch.cuda.synchronize()
+        pre0 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+        dec0 = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+        w0 = w.with_counts(0, 0, 0)
+        out["dense_baseline"] = {
+            "decode_us": round(dec0 * 1e6, 2),
+            "decode_gbs": round(decode_bytes(w0, G) / dec0 / 1e9, 1),
+            "prefill_ms": round(pre0 * 1e3, 3),
+            "prefill_tflops": round(4 * w.D * w.L * (w.L + 1) / 2 * w.hq * w.b / pre0 / 1e12, 1)}
+        out["speedup_vs_dense"] = {"decode": round(dec0 / dec_s, 3),
+                                   "prefill": round(pre0 / pre_s, 3),
+                                   "decode_ideal_bytes": round(decode_bytes(w0, G) / d_bytes, 3),
+                                   "prefill_ideal_flops": round(
+                                       4 * w.D * w.L * (w.L + 1) / 2 * w.hq * w.b / executed, 3)}
+        del cache0
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
