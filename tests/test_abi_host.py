@@ -1,0 +1,178 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry point the
+header declares, computes buffer sizes that match the oracle's closed-form pool sizes, and rejects
+every invalid argument before anything is launched.
+
+Only argument combinations that fail host validation are passed with placeholder pointers, so no
+call here reaches a HIP launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle import Dims
+from sparse_kv_cache_magnitude_amd import hierasparse as hs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hierasparse.h")
+
+FAKE = 1 << 20          # aligned placeholder address, never dereferenced (validation fails first)
+MISALIGNED = FAKE + 8
+
+
+def declared_entry_points():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_entry_points() == sorted(hs.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hs.LIB_PATH)
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("b,hq,hkv,L,B,counts", [
+    (8, 32, 8, 32768, 64, (77, 307, 307)),
+    (1, 32, 8, 16384, 128, (0, 90, 90)),
+    (4, 32, 8, 131072, 64, (819, 1024, 1024)),
+    (3, 6, 2, 9 * 64, 64, (2, 3, 7)),
+])
+def test_cache_sizes_match_oracle_pools(b, hq, hkv, L, B, counts):
+    got = hs.hs_cache_sizes(hs.shape(b, hq, hkv, L, 128, B), hs.counts(*counts))
+    want = oracle.pool_bytes(Dims(b, hkv, L, 128, B, *counts))
+    assert got == want
+
+
+def test_workspace_sizes():
+    shp, cnt = hs.shape(2, 8, 2, 1024, 128, 64), hs.counts(1, 3, 4)
+    assert hs.hs_workspace_size(hs.HS_OP_COMPRESS, shp, cnt) == 2 * 2 * 16 * 3 * 8
+    for s in (1, 7, 512):
+        # fp32 partial output (head_dim) and log-sum-exp per (batch, query head, split)
+        assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) == 2 * 8 * s * (128 + 1) * 4
+    assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, 0) > 0
+
+
+def _status(call):
+    try:
+        call()
+    except hs.HsError as e:
+        return e.status
+    return hs.HS_OK
+
+
+BAD_SHAPES = [
+    (hs.shape(1, 4, 1, 1024, 64, 64), hs.HS_ERR_SHAPE),       # head_dim != 128
+    (hs.shape(1, 4, 1, 1024, 128, 32), hs.HS_ERR_SHAPE),      # block not 64/128
+    (hs.shape(1, 4, 1, 1000, 128, 64), hs.HS_ERR_SHAPE),      # seq_len % block
+    (hs.shape(1, 6, 4, 1024, 128, 64), hs.HS_ERR_SHAPE),      # q_heads % kv_heads
+    (hs.shape(0, 4, 1, 1024, 128, 64), hs.HS_ERR_SHAPE),      # empty batch
+    (hs.shape(1, 4, 1, 64 * 4097, 128, 64), hs.HS_ERR_SHAPE),  # too many blocks per head
+]
+
+
+@pytest.mark.parametrize("shp,code", BAD_SHAPES)
+def test_bad_shapes_rejected_by_every_entry_point(shp, code):
+    cnt = hs.counts(0, 0, 0)
+    assert _status(lambda: hs.hs_cache_sizes(shp, cnt)) == code
+    assert _status(lambda: hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt)) == code
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    assert _status(lambda: _compress(shp, cnt, FAKE, FAKE, cache, FAKE, 1 << 30)) == code
+    assert _status(lambda: _decode(shp, cnt, cache, FAKE, FAKE, None, 0, FAKE, 1 << 30)) == code
+    assert _status(lambda: _prefill(shp, cnt, cache, FAKE, FAKE, None, 0)) == code
+    assert hs.hs_last_error() != ""
+
+
+@pytest.mark.parametrize("counts", [(-1, 0, 0), (0, 17, 0), (8, 0, 9), (16, 1, 0)])
+def test_bad_counts_rejected(counts):
+    shp = hs.shape(1, 4, 1, 1024, 128, 64)   # 16 blocks per head
+    assert _status(lambda: hs.hs_cache_sizes(shp, hs.counts(*counts))) == hs.HS_ERR_COUNTS
+
+
+# ---- raw calls with placeholder addresses (validation must fail before any launch) ----------
+
+def _cache_struct(cache):
+    return hs.HsCache(*[ctypes.c_void_p(cache[f]) if cache.get(f) else None
+                        for f in hs.CACHE_FIELDS])
+
+
+def _raise(st):
+    if st != hs.HS_OK:
+        raise hs.HsError(st, hs.hs_last_error())
+
+
+def _compress(shp, cnt, k, v, cache, ws, ws_bytes):
+    _raise(hs.lib().hs_compress(ctypes.byref(shp), ctypes.byref(cnt), k, v,
+                                ctypes.byref(_cache_struct(cache)), ws, ws_bytes, None))
+
+
+def _decode(shp, cnt, cache, q, o, lse, splits, ws, ws_bytes):
+    _raise(hs.lib().hs_decode_attn(ctypes.byref(shp), ctypes.byref(cnt),
+                                   ctypes.byref(_cache_struct(cache)), q, o, lse, 0.0, splits,
+                                   ws, ws_bytes, None))
+
+
+def _prefill(shp, cnt, cache, q, o, lse, flags):
+    _raise(hs.lib().hs_prefill_attn(ctypes.byref(shp), ctypes.byref(cnt),
+                                    ctypes.byref(_cache_struct(cache)), q, o, lse, 0.0, flags,
+                                    None))
+
+
+SHP, CNT = hs.shape(1, 4, 1, 1024, 128, 64), hs.counts(2, 4, 5)
+
+
+def test_null_pointers_rejected():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    assert _status(lambda: _compress(SHP, CNT, None, FAKE, cache, FAKE, 1 << 30)) == hs.HS_ERR_NULL
+    assert _status(lambda: _compress(SHP, CNT, FAKE, None, cache, FAKE, 1 << 30)) == hs.HS_ERR_NULL
+    for f in hs.CACHE_FIELDS:
+        c = dict(cache, **{f: None})
+        assert _status(lambda: _compress(SHP, CNT, FAKE, FAKE, c, FAKE, 1 << 30)) == hs.HS_ERR_NULL
+        assert _status(lambda: _decode(SHP, CNT, c, FAKE, FAKE, None, 0, FAKE, 1 << 30)) \
+            == hs.HS_ERR_NULL
+        assert _status(lambda: _prefill(SHP, CNT, c, FAKE, FAKE, None, 0)) == hs.HS_ERR_NULL
+    assert _status(lambda: _decode(SHP, CNT, cache, None, FAKE, None, 0, FAKE, 1 << 30)) \
+        == hs.HS_ERR_NULL
+    assert _status(lambda: _prefill(SHP, CNT, cache, FAKE, None, None, 0)) == hs.HS_ERR_NULL
+
+
+def test_misaligned_pointers_rejected():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    assert _status(lambda: _compress(SHP, CNT, MISALIGNED, FAKE, cache, FAKE, 1 << 30)) \
+        == hs.HS_ERR_ALIGN
+    c = dict(cache, v_meta=MISALIGNED)
+    assert _status(lambda: _decode(SHP, CNT, c, FAKE, FAKE, None, 0, FAKE, 1 << 30)) \
+        == hs.HS_ERR_ALIGN
+    assert _status(lambda: _prefill(SHP, CNT, cache, FAKE, FAKE, MISALIGNED, 0)) \
+        == hs.HS_ERR_ALIGN
+
+
+def test_workspace_checks():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    need = hs.hs_workspace_size(hs.HS_OP_COMPRESS, SHP, CNT)
+    assert _status(lambda: _compress(SHP, CNT, FAKE, FAKE, cache, FAKE, need - 1)) \
+        == hs.HS_ERR_WORKSPACE
+    assert _status(lambda: _compress(SHP, CNT, FAKE, FAKE, cache, None, need)) \
+        == hs.HS_ERR_WORKSPACE
+    need = hs.hs_workspace_size(hs.HS_OP_DECODE, SHP, CNT, 3)
+    assert _status(lambda: _decode(SHP, CNT, cache, FAKE, FAKE, None, 3, FAKE, need - 4)) \
+        == hs.HS_ERR_WORKSPACE
+    assert _status(lambda: _decode(SHP, CNT, cache, FAKE, FAKE, None, 513, FAKE, 1 << 30)) \
+        == hs.HS_ERR_SHAPE
+
+
+def test_unknown_flags_and_ops():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    assert _status(lambda: _prefill(SHP, CNT, cache, FAKE, FAKE, None, 7)) == hs.HS_ERR_UNSUPPORTED
+    assert _status(lambda: hs.hs_workspace_size(9, SHP, CNT)) == hs.HS_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for code in range(8):
+        assert hs.hs_status_string(code) not in ("", "unknown status")
