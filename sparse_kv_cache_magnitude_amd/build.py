@@ -29,9 +29,16 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source extra flags. The prefill kernel mixes dense MFMA and SMFMAC on the same accumulators;
+# SMFMAC's accumulator is always a VGPR tuple, so dense MFMAs there use the VGPR form as well (no
+# copies between accumulation and arch registers).
+EXTRA = {"hs_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
