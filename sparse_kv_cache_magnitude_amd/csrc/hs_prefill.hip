@@ -12,21 +12,23 @@
 // workgroups of one KV head run on one XCD. Two waves per SIMD let one wave's matrix-core work
 // overlap the other's softmax.
 //
-// Per visible 64-token KV tile n (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 for dense,
-// v_smfmac_f32_32x32x32_bf16 for 2:4 operands; all accumulators in VGPRs):
-//   staging   four 32 KB LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4)
-//             two tiles ahead; one barrier per tile. A stage holds the tile's K and V^T exactly in
-//             their stored representation (dense copy, or kept values + metadata).
+// Per visible 64-token KV tile n (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 and
+// v_smfmac_f32_32x32x32_bf16; all accumulators in VGPRs):
+//   staging   four LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) two
+//             tiles ahead; one barrier per tile. A stage holds the tile's K and V^T in their stored
+//             representation (dense copy, or kept values + metadata), rows padded by 16 bytes so
+//             that the operand reads are free of bank conflicts with plain immediate offsets.
 //   GEMM1     S^T[64 tok][32 q] = K Q^T (Q stays in registers as the B operand).
 //   softmax   causal mask, column-wise running max (exp2 domain, lazy rescale) and
 //             P^T = exp2(S^T - max) packed to bf16 in registers.
 //   GEMM2     O^T[128 ch][32 q] += V^T P^T, for tile n-1, interleaved with the softmax of tile n.
-// Token order: GEMM1's A operand rows are the tile's tokens in the order tau (bits 2 and 3 of the
-// row index exchanged). The 32x32 accumulator then holds, in lane half h, tokens 8h..8h+7 and
-// 16+8h..16+8h+7 of each 32-token half in consecutive registers, which is exactly GEMM2's B operand
-// layout (lane half h, k = 8h + e): P^T needs no data movement between lanes.
-// 2:4 tiles go to SMFMAC, or (decompress variant) are expanded in registers from the same LDS
-// stage into dense MFMA operands.
+// Token order: GEMM1's A operand rows are the tile's tokens in an order tau chosen so that the
+// 32x32 accumulator lands exactly in GEMM2's B operand layout (lane half h holds 16 consecutive
+// registers per 32-token half); P^T needs no data movement between lanes. The stage stores the K
+// rows already in that order.
+// SMFMAC path: 2:4 operands go to v_smfmac; dense V^T is fed to the same instruction as two 2:4
+// halves (so the output accumulators see one instruction type). Decompress path: 2:4 operands are
+// expanded in registers from the same LDS stage and everything runs on dense MFMA.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -34,26 +36,44 @@ namespace hs {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kTile = 64;                                 // KV tokens per tile
-constexpr int kQTile = 32;                                // queries per wave
+constexpr int kTile = 64;   // KV tokens per tile
+constexpr int kQTile = 32;  // queries per wave
 constexpr int kWaves = 8;
 constexpr int kStages = 4;
-constexpr int kStageBytes = 32 * 1024;                    // K region 16 KB + V region 16 KB
-constexpr int kVRegion = 16 * 1024;
-constexpr int kMetaOff = 8 * 1024;                        // metadata of a 2:4 K or V tile
-constexpr int kMapOff = kStages * kStageBytes;            // per-block local slots, int16
-constexpr int kLdsBytes = kMapOff + 2 * kMaxBlocks * 2;   // 144 KB
-constexpr float kTau = 8.0f;                              // lazy-rescale threshold (log2 units)
+
+// ---- LDS stage layout (bytes). Rows are padded by one 16-byte unit: with a stride of 17, 9 or 5
+// units, 16 consecutive rows read at one column hit 16 distinct bank groups.
+constexpr int kKdStride = 272;                    // dense K row: 64 tok x (256 + 16)
+constexpr int kKnStride = 144;                    // 2:4 K values row: 64 tok x (128 + 16)
+constexpr int kVdStride = 144;                    // dense V^T row: 128 ch x (128 + 16)
+constexpr int kVnStride = 80;                     // 2:4 V^T values row: 128 ch x (64 + 16)
+constexpr int kKdUnits = 64 * kKdStride / 16;     // 1088 sixteen-byte units (17 loads)
+constexpr int kKnUnits = 64 * kKnStride / 16;     // 576 (9 loads)
+constexpr int kVdUnits = 128 * kVdStride / 16;    // 1152 (18 loads)
+constexpr int kVnUnits = 128 * kVnStride / 16;    // 640 (10 loads)
+constexpr int kKMetaOff = kKnUnits * 16;          // 2:4 K metadata: 64 tok x 16 B
+constexpr int kVMetaOff = kVnUnits * 16;          // 2:4 V metadata: 128 ch x 8 B
+constexpr int kKRegion = kKdUnits * 16;           // 17408
+constexpr int kVRegion = kVdUnits * 16;           // 18432
+constexpr int kStageBytes = kKRegion + kVRegion;  // 35840
+constexpr int kMapOff = kStages * kStageBytes;    // per-block local slots, int16
+constexpr int kLdsBytes = kMapOff + 2 * kMaxBlocks * 2;  // 156 KB
+static_assert(kKdUnits % 64 == 0 && kVdUnits % 64 == 0 && kKnUnits % 64 == 0 &&
+                  kVnUnits % 64 == 0, "whole 1 KB loads");
+static_assert(kKMetaOff + 1024 <= kKRegion && kVMetaOff + 1024 <= kVRegion, "metadata fits");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// ---- LDS swizzles (16-byte chunk index XOR a function of the row) ------------------------------
-// Every 16-lane group of an operand read touches 16 rows at one logical chunk; the functions below
-// make the physical chunks distinct within every 8 and every 16 consecutive lanes.
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
-__device__ __forceinline__ int fv(int x) { return (x & 7) ^ ((x >> 3) & 1); }   // 128-byte rows
-__device__ __forceinline__ int gv(int x) { return ((x >> 1) ^ (x >> 2)) & 3; }  // 64-byte rows
+__device__ __forceinline__ int swap13(int x) { return (x & ~10) | ((x & 2) << 2) | ((x & 8) >> 2); }
+// Token held by GEMM1 row r (0..31) of a 32-token half: bits 2,3 of r exchanged when the tile's V
+// is consumed in natural order (dense MFMA k-steps, or stored 2:4 groups), bits 1,3 exchanged when
+// a dense V tile is split into two 2:4 halves for SMFMAC (see gemm2_smfmac_step).
+__device__ __forceinline__ int tau(int r, bool split) { return split ? swap13(r) : swap23(r); }
 
 // ---- direct global -> LDS loads -----------------------------------------------------------------
 // Lane i of the wave writes LDS[lds_addr + size * i]; the global address is gbase + voff (per lane).
@@ -83,12 +103,15 @@ __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t 
       : "v"(voff), "s"(gbase), "s"(lds_addr)
       : "memory");
 }
-// Wait until at most n of this wave's vector-memory operations are outstanding (n in 0..4).
+// Wait until at most n of this wave's vector-memory operations are outstanding (n in 0..6).
 __device__ __forceinline__ void wait_vmem(int n) {
   switch (n) {
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
     case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
     case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
@@ -153,45 +176,48 @@ struct PrefillArgs {
 
 // Per-wave state of the online softmax and the output accumulators (one 32-query tile).
 struct WaveState {
-  bf16x16 qv[4];    // Q^T as GEMM1 B operand, per 32 channels (two 16-channel dense k-steps)
-  f32x16 o[4];      // O^T, per 32-channel tile
-  f32x16 s[2];      // S^T of the current tile, per 32-token half
-  bf16x16 p[2];     // P^T per 32 tokens (two 16-token dense k-steps): previous tile until
-                    // overwritten by the current one
+  bf16x16 qv[4];  // Q^T as GEMM1 B operand, per 32 channels (two 16-channel dense k-steps)
+  f32x16 o[4];    // O^T, per 32-channel tile
+  f32x16 s[2];    // S^T of the current tile, per 32-token half
+  bf16x16 p[2];   // P^T per 32 tokens (two 16-token dense k-steps): previous tile until
+                  // overwritten by the current one
   float m_run, l_run, m_use, alpha;
 };
 
+// Per-lane LDS byte offsets of the operand reads, relative to a stage.
+struct LaneOffsets {
+  int kd, kn, km;  // dense K rows, 2:4 K values, 2:4 K metadata
+  int vd, vn, vm;  // dense V^T rows, 2:4 V^T values, 2:4 V^T metadata
+};
+
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
+// Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
 template <bool kSparseK, bool kSmfmac>
-__device__ __forceinline__ void gemm1(WaveState &w, const char *kl, int r, int hf) {
+__device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOffsets &lo,
+                                      int hf) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     f32x16 acc = zero16();
-    const int row = 32 * T + swap23(r);
     if (!kSparseK) {
-      const char *rp = kl + row * 256;
+      const char *rp = st + lo.kd + T * 32 * kKdStride;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 k = as_bf16x8(lds16(rp + (((2 * ks + hf) ^ (r & 15)) << 4)));
-        acc = mfma32(k, half8(w.qv[ks >> 1], ks & 1), acc);
-      }
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma32(as_bf16x8(lds16(rp + 32 * ks)), half8(w.qv[ks >> 1], ks & 1), acc);
     } else {
-      const char *rp = kl + row * 128;
-      const uint4 meta = lds16(kl + kMetaOff + (32 * T + r) * 16);
+      const char *rp = st + lo.kn + T * 32 * kKnStride;
+      const uint4 meta = lds16(st + lo.km + T * 32 * 16);
       const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
-      const int f = fv(r & 15);
       if (kSmfmac) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 k = as_bf16x8(lds16(rp + (((2 * u + hf) ^ f) << 4)));
-          acc = smfmac32(k, w.qv[u], mw[u] >> (16 * hf), acc);
-        }
+        for (int u = 0; u < 4; ++u)
+          acc = smfmac32(as_bf16x8(lds16(rp + 32 * u)), w.qv[u], mw[u] >> (16 * hf), acc);
       } else {
+        // Decompress: the lane's 8-byte half of 16-byte unit ks (lo.kn carries +16 per half).
+        const char *rq = rp - 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const uint2 v = lds8(rp + ((ks ^ f) << 4) + 8 * hf);
           const uint32_t bits = (mw[ks >> 1] >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          acc = mfma32(expand2(v, bits), half8(w.qv[ks >> 1], ks & 1), acc);
+          acc = mfma32(expand2(lds8(rq + 16 * ks), bits), half8(w.qv[ks >> 1], ks & 1), acc);
         }
       }
     }
@@ -199,56 +225,68 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *kl, int r, int h
   }
 }
 
-// ---- GEMM2: O^T += V^T P^T for one staged tile, P^T of that tile in w.p ------------------------
-template <bool kSparseV, bool kSmfmac>
-__device__ __forceinline__ void gemm2(WaveState &w, const char *vl, int r, int hf) {
+// ---- GEMM2 on the SMFMAC path, one 32-token k-step u ------------------------------------------
+// Dense and 2:4 V^T tiles share one instruction sequence, so O^T stays in one register set: per
+// 32-channel tile, one SMFMAC on the kept values (2:4: stored values and metadata; dense: the
+// lane's tokens 0..7 at group positions {0,1}, index 0x4444), and for a dense tile a second one on
+// tokens 8..15 at positions {2,3} (index 0xEEEE). For a dense tile P^T arrives in the matching
+// token order (tau with bits 1 and 3 exchanged).
+__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, const char *st, bool sparse,
+                                                  const uint2 *meta, int u, const LaneOffsets &lo,
+                                                  int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const int ch = 32 * ct + r;
+    const char *a = sparse ? st + lo.vn + ct * 32 * kVnStride + 32 * u
+                           : st + lo.vd + ct * 32 * kVdStride + 64 * u;
+    const uint32_t idx = sparse ? ((u ? meta[ct].y : meta[ct].x) >> (16 * hf)) : 0x4444u;
+    w.o[ct] = smfmac32(as_bf16x8(lds16(a)), w.p[u], idx, w.o[ct]);
+    if (!sparse) w.o[ct] = smfmac32(as_bf16x8(lds16(a + 16)), w.p[u], 0xEEEEu, w.o[ct]);
+  }
+}
+__device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
+                                           const LaneOffsets &lo) {
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+    meta[ct] = sparse ? lds8(st + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
+}
+
+// ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
+template <bool kSparseV>
+__device__ __forceinline__ void gemm2_dense_step(WaveState &w, const char *st, const uint2 *meta,
+                                                 int ks, const LaneOffsets &lo, int hf) {
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    bf16x8 v;
     if (!kSparseV) {
-      const char *rp = vl + ch * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 v = as_bf16x8(lds16(rp + (((2 * ks + hf) ^ fv(r & 15)) << 4)));
-        w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
-      }
+      // lo.vd carries +32 for lane half 1 (the split layout); a dense k-step wants +16.
+      v = as_bf16x8(lds16(st + lo.vd - 16 * hf + ct * 32 * kVdStride + 32 * ks));
     } else {
-      const char *rp = vl + ch * 64;
-      const uint2 meta = lds8(vl + kMetaOff + ch * 8);
-      const int g = gv(r);
-      if (kSmfmac) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 v = as_bf16x8(lds16(rp + (((2 * u + hf) ^ g) << 4)));
-          w.o[ct] = smfmac32(v, w.p[u], (u ? meta.y : meta.x) >> (16 * hf), w.o[ct]);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint2 v = lds8(rp + ((ks ^ g) << 4) + 8 * hf);
-          const uint32_t bits = (((ks >> 1) ? meta.y : meta.x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          w.o[ct] = mfma32(expand2(v, bits), half8(w.p[ks >> 1], ks & 1), w.o[ct]);
-        }
-      }
+      const uint32_t bits =
+          (((ks >> 1) ? meta[ct].y : meta[ct].x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
+      v = expand2(lds8(st + lo.vn - 8 * hf + ct * 32 * kVnStride + 16 * ks), bits);
     }
+    w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
   }
 }
 
 // ---- softmax of the current tile: causal mask, running max, decision to rescale ----------------
 // 'shift' = (first token of the key tile) - (first query of the wave); a token is masked when
 // shift + token > query. Returns true if the running max moves (then w.alpha rescales O and l).
-__device__ __forceinline__ bool softmax_max(WaveState &w, bool diag, int shift, int r, int hf,
-                                            float c) {
+__device__ __forceinline__ bool softmax_max(WaveState &w, bool diag, bool split, int shift, int r,
+                                            int hf, float c) {
+  if (diag) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (shift + 32 * T + tau(8 * (e >> 2) + 4 * hf + (e & 3), split) > r)
+          w.s[T][e] = -INFINITY;
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int T = 0; T < 2; ++T)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = w.s[T][e];
-      if (diag && shift + 32 * T + 16 * (e >> 3) + 8 * hf + (e & 7) > r) x = -INFINITY;
-      w.s[T][e] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, w.s[T][e]);
   const float mt = max_halves(mx) * c;
   const float m_new = fmaxf(w.m_run, mt);
   const bool need = __builtin_amdgcn_ballot_w64(m_new > w.m_run + kTau) != 0;
@@ -262,9 +300,9 @@ __device__ __forceinline__ bool softmax_max(WaveState &w, bool diag, int shift, 
   return need;
 }
 
-// P^T of the current tile for GEMM2 k-step ks (tokens 16ks .. 16ks+15): the accumulator
-// registers 8*(ks&1) .. +7 of half ks>>1, exponentiated and packed to bf16. The bf16 values are
-// also summed (dot product with ones) into the running denominator.
+// P^T of the current tile for GEMM2 k-step ks (16 tokens): the accumulator registers
+// 8*(ks&1) .. +7 of half ks>>1, exponentiated and packed to bf16. The bf16 values are also summed
+// (dot product with ones) into the running denominator.
 __device__ __forceinline__ void softmax_exp(WaveState &w, int ks, float c, float mc, float &lsum) {
   const f32x16 &s = w.s[ks >> 1];
   const int base = 8 * (ks & 1);
@@ -296,58 +334,53 @@ __device__ __forceinline__ void softmax_finish(WaveState &w, bool need, float ls
   }
 }
 
-// Exponentials of the current tile interleaved with GEMM2 of the previous tile, one 16-token
-// k-step at a time (two for SMFMAC): the MFMAs that read P^T[ks] of the previous tile are issued,
-// then the same registers receive P^T[ks] of the current tile. Only the V operands of one k-step
-// are live at a time.
-template <bool kGemm2, bool kSparseV, bool kSmfmac>
-__device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *vl, int r, int hf,
+template <bool kSmfmac>
+__device__ __forceinline__ void gemm2_u(WaveState &w, const char *st, bool sparse,
+                                        const uint2 *meta, int u, const LaneOffsets &lo, int hf) {
+  if (kSmfmac) {
+    gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
+  } else if (sparse) {
+    gemm2_dense_step<true>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<true>(w, st, meta, 2 * u + 1, lo, hf);
+  } else {
+    gemm2_dense_step<false>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<false>(w, st, meta, 2 * u + 1, lo, hf);
+  }
+}
+
+// Exponentials of the current tile interleaved with GEMM2 of the previous tile (if 'gemm'): the
+// instructions that read P^T of the previous tile are issued first, then the same registers
+// receive P^T of the current tile, 32 tokens at a time.
+template <bool kSmfmac>
+__device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev, bool gemm,
+                                               bool sparse, const LaneOffsets &lo, int hf,
                                                float c) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
-  if (!kGemm2) {
+  uint2 meta[4];
+  load_vmeta(meta, st_prev, gemm && sparse, lo);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
-  } else if (!kSparseV) {
-    const int f = fv(r & 15);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bf16x8 v = as_bf16x8(lds16(vl + (32 * ct + r) * 128 + (((2 * ks + hf) ^ f) << 4)));
-        w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
-      }
-      softmax_exp(w, ks, c, mc, lsum);
-    }
-  } else {
-    uint2 meta[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) meta[ct] = lds8(vl + kMetaOff + (32 * ct + r) * 8);
-    const int g = gv(r);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const char *rp = vl + (32 * ct + r) * 64;
-        const uint32_t mw = u ? meta[ct].y : meta[ct].x;
-        if (kSmfmac) {
-          const bf16x8 v = as_bf16x8(lds16(rp + (((2 * u + hf) ^ g) << 4)));
-          w.o[ct] = smfmac32(v, w.p[u], mw >> (16 * hf), w.o[ct]);
-        } else {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const int ks = 2 * u + k2;
-            const uint2 v = lds8(rp + ((ks ^ g) << 4) + 8 * hf);
-            w.o[ct] = mfma32(expand2(v, (mw >> (16 * k2 + 8 * hf)) & 0xFFu), half8(w.p[u], k2),
-                             w.o[ct]);
-          }
-        }
-      }
-      softmax_exp(w, 2 * u, c, mc, lsum);
-      softmax_exp(w, 2 * u + 1, c, mc, lsum);
-    }
+  for (int u = 0; u < 2; ++u) {
+    if (gemm) gemm2_u<kSmfmac>(w, st_prev, sparse, meta, u, lo, hf);
+    softmax_exp(w, 2 * u, c, mc, lsum);
+    softmax_exp(w, 2 * u + 1, c, mc, lsum);
   }
   return lsum;
+}
+
+// ---- staging of one tile -----------------------------------------------------------------------
+// Each region is a whole number of 1 KB loads (64 lanes x 16 B of the padded layout); load q of a
+// region goes to wave q % 8. Pad units receive a copy of a real unit of the same row. Metadata:
+// K (1 KB) by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves
+// 3-6 (block 128, where a tile is half of each channel's metadata row).
+template <int B>
+__device__ __forceinline__ int dma_count(int wave, bool dense_k, bool dense_v) {
+  const int k = dense_k ? (kKdUnits / 64 + 7 - wave) / 8
+                        : (kKnUnits / 64 + 7 - wave) / 8 + (wave == 1 ? 1 : 0);
+  const int v = dense_v ? (kVdUnits / 64 + 7 - wave) / 8
+                        : (kVnUnits / 64 + 7 - wave) / 8 +
+                              (B == 64 ? (wave == 2 ? 1 : 0) : (wave >= 3 && wave <= 6 ? 1 : 0));
+  return k + v;
 }
 
 template <int B, bool kSmfmac>
@@ -404,68 +437,75 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   w.m_run = -INFINITY;
   w.l_run = 0.f;
 
+  LaneOffsets lo;
+  lo.kd = r * kKdStride + 16 * hf;
+  lo.kn = r * kKnStride + 16 * hf;
+  lo.km = kKMetaOff + r * 16;
+  lo.vd = kKRegion + r * kVdStride + 32 * hf;
+  lo.vn = kKRegion + r * kVnStride + 16 * hf;
+  lo.vm = kKRegion + kVMetaOff + r * 8;
+
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
 
   __syncthreads();  // block modes visible
 
+  auto mode_k = [&](int kt) { return __builtin_amdgcn_readfirstlane(mk16[kt / TPB]); };
+  auto mode_v = [&](int kt) { return __builtin_amdgcn_readfirstlane(mv16[kt / TPB]); };
   auto next_visible = [&](int kt) {
-    while (kt <= kt_max && mk16[kt / TPB] == 0) ++kt;
+    while (kt <= kt_max && mode_k(kt) == 0) ++kt;
     return kt;
   };
-  auto dma_count = [&](int kt) {
-    const int blk = kt / TPB;
-    return (mk16[blk] > 0 ? 2 : 1 + (wave < 4)) + (mv16[blk] > 0 ? 2 : 1 + (wave >= 4));
-  };
-  // Direct loads of one tile into a stage. Instruction q of a region writes LDS bytes
-  // 1024*q .. +1023 (lane i: bytes 16*i .. +15); metadata goes as 256-byte dword loads (lane i:
-  // bytes 4*i .. +3), K metadata by waves 0-3 and V metadata by waves 4-7. The per-lane global
-  // byte offsets implement the LDS swizzles; they are recomputed here rather than kept live.
+  // Direct loads of one tile into a stage. The per-lane global offsets are recomputed here (from
+  // an opaque copy of the lane index) rather than kept live across the loop.
   auto issue = [&](int kt, int stage) {
-    const int blk = kt / TPB, half = kt % TPB;
-    const int mk = __builtin_amdgcn_readfirstlane(mk16[blk]);
-    const int mv = __builtin_amdgcn_readfirstlane(mv16[blk]);
-    const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kVRegion;
+    const int half = kt % TPB;
+    const int mk = mode_k(kt), mv = mode_v(kt);
+    const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kKRegion;
+    const bool split = kSmfmac && mv > 0;  // GEMM1 row order of this tile (see tau)
     int ln = lane;
-    asm volatile("" : "+v"(ln));  // keep the offset arithmetic here instead of hoisted and spilled
-    const int p1 = 64 * wave + ln;     // slot of a single-instruction region
-    const int dm = 64 * (wave & 3) + ln;  // dword slot of a metadata region
+    asm volatile("" : "+v"(ln));
+    auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, split); };
     if (mk > 0) {
       const char *g = uniform_ptr(
           a.c.k_dense + ((size_t)(head * a.ndk + mk - 1) * B + kTile * half) * kD);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int p = 64 * (2 * wave + m) + ln, row = p >> 4;
-        dma16(g, row * 256 + (((p & 15) ^ swap23(row & 15)) << 4), kl + 1024 * (2 * wave + m));
+      for (int q = wave; q < kKdUnits / 64; q += kWaves) {
+        const int u = 64 * q + ln, row = u / 17, cu = u - 17 * row;
+        dma16(g, token(row) * 256 + 16 * min(cu, 15), kl + 1024 * q);
       }
     } else {
       const size_t row0 = (size_t)(head * a.nsk - mk - 1) * B + kTile * half;
-      const int t = p1 >> 3;
-      dma16(uniform_ptr(a.c.k_nnz + row0 * (kD / 2)),
-            t * 128 + (((p1 & 7) ^ fv(swap23(t & 15))) << 4), kl + 1024 * wave);
-      if (wave < 4) {
-        const int sl = dm >> 2, tok = (sl & ~15) | swap23(sl & 15);
-        dma4(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), tok * 16 + (dm & 3) * 4,
-             kl + kMetaOff + 256 * wave);
+      const char *g = uniform_ptr(a.c.k_nnz + row0 * (kD / 2));
+      for (int q = wave; q < kKnUnits / 64; q += kWaves) {
+        const int u = 64 * q + ln, row = u / 9, cu = u - 9 * row;
+        dma16(g, token(row) * 128 + 16 * min(cu, 7), kl + 1024 * q);
       }
+      if (wave == 1)
+        dma16(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), token(ln) * 16, kl + kKMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(a.c.v_dense + (size_t)(head * a.ndv + mv - 1) * B * kD +
                                   kTile * half);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int p = 64 * (2 * wave + m) + ln, ch = p >> 3;
-        dma16(g, ch * (2 * B) + (((p & 7) ^ fv(ch & 15)) << 4), vl + 1024 * (2 * wave + m));
+      for (int q = wave; q < kVdUnits / 64; q += kWaves) {
+        const int u = 64 * q + ln, ch = u / 9, cu = u - 9 * ch;
+        dma16(g, ch * (2 * B) + 16 * min(cu, 7), vl + 1024 * q);
       }
     } else {
       const size_t blk0 = (size_t)(head * a.nsv - mv - 1) * B * kD;
-      const int ch = p1 >> 2;
-      dma16(uniform_ptr(a.c.v_nnz + blk0 / 2 + (kTile / 2) * half),
-            ch * B + (((p1 & 3) ^ gv(ch)) << 4), vl + 1024 * wave);
-      if (wave >= 4)
-        dma4(uniform_ptr(a.c.v_meta + blk0 / 16 + (kTile / 16) * half),
-             (dm >> 1) * (B / 8) + (dm & 1) * 4, vl + kMetaOff + 256 * (wave - 4));
+      const char *g = uniform_ptr(a.c.v_nnz + blk0 / 2 + (kTile / 2) * half);
+      for (int q = wave; q < kVnUnits / 64; q += kWaves) {
+        const int u = 64 * q + ln, ch = u / 5, cu = u - 5 * ch;
+        dma16(g, ch * B + 16 * min(cu, 3), vl + 1024 * q);
+      }
+      const char *gm = uniform_ptr(a.c.v_meta + blk0 / 16 + (kTile / 16) * half);
+      if (B == 64) {
+        if (wave == 2) dma16(gm, 16 * ln, vl + kVMetaOff);
+      } else if (wave >= 3 && wave <= 6) {
+        const int d = 64 * (wave - 3) + ln;  // dword d: channel d/2, dword d%2 of its 8 bytes
+        dma4(gm, (d >> 1) * (B / 8) + 4 * (d & 1), vl + kVMetaOff + 256 * (wave - 3));
+      }
     }
   };
+  auto count_of = [&](int kt) { return dma_count<B>(wave, mode_k(kt) > 0, mode_v(kt) > 0); };
 
   const float c = a.scale_log2;
   int kt0 = next_visible(0);
@@ -476,42 +516,36 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
   bool prev_sparse_v = false;
-  const char *vl_prev = lds;
+  const char *st_prev = lds;
   int it = 0;
   while (kt0 <= kt_max) {
     const int kt2 = kt1 <= kt_max ? next_visible(kt1 + 1) : kt_max + 1;
-    wait_vmem(kt1 <= kt_max ? dma_count(kt1) : 0);
+    wait_vmem(kt1 <= kt_max ? count_of(kt1) : 0);
     barrier();  // tile kt0 staged by every wave; stage (it + 2) % 4 no longer read
     if (kt2 <= kt_max) issue(kt2, (it + 2) & 3);
 
-    const char *kl = lds + (it & 3) * kStageBytes, *vl = kl + kVRegion;
-    const int blk = kt0 / TPB;
-    const bool sparse_k = mk16[blk] < 0, sparse_v = mv16[blk] < 0;
+    const char *st = lds + (it & 3) * kStageBytes;
+    const bool sparse_k = mode_k(kt0) < 0, sparse_v = mode_v(kt0) < 0;
     if (sparse_k)
-      gemm1<true, kSmfmac>(w, kl, r, hf);
+      gemm1<true, kSmfmac>(w, st, lo, hf);
     else
-      gemm1<false, kSmfmac>(w, kl, r, hf);
+      gemm1<false, kSmfmac>(w, st, lo, hf);
     const int shift = kTile * kt0 - kQTile * qt;
-    const bool need = softmax_max(w, shift > -kTile, shift, r, hf, c);
-    float lsum;
-    if (it == 0)
-      lsum = exp_and_gemm2<false, false, kSmfmac>(w, vl_prev, r, hf, c);
-    else if (prev_sparse_v)
-      lsum = exp_and_gemm2<true, true, kSmfmac>(w, vl_prev, r, hf, c);
-    else
-      lsum = exp_and_gemm2<true, false, kSmfmac>(w, vl_prev, r, hf, c);
+    const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
+    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c);
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
-    vl_prev = vl;
+    st_prev = st;
     kt0 = kt1;
     kt1 = kt2;
     ++it;
   }
-  if (it > 0) {  // GEMM2 of the last tile (its stage is not overwritten after the loop)
-    if (prev_sparse_v)
-      gemm2<true, kSmfmac>(w, vl_prev, r, hf);
-    else
-      gemm2<false, kSmfmac>(w, vl_prev, r, hf);
+  // GEMM2 of the last tile (its stage is not overwritten after the loop).
+  if (it > 0) {
+    uint2 meta[4];
+    load_vmeta(meta, st_prev, prev_sparse_v, lo);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
   }
 
   if (!has_task) return;
