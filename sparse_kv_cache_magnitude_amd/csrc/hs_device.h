@@ -49,11 +49,12 @@ __device__ __forceinline__ f32x4 smfmac16(uint4 a, uint4 b_lo, uint4 b_hi, uint3
                                                     (int)idx, 0, 0);
 }
 
-// Two fp32 -> packed bf16x2 (round to nearest even, gfx950 v_cvt_pk_bf16_f32).
+// Two fp32 -> packed bf16x2 (round to nearest even, one gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ----------------------------------------------------------------------------------------------

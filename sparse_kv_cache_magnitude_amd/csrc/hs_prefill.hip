@@ -200,17 +200,23 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOf
     f32x16 acc = zero16();
     if (!kSparseK) {
       const char *rp = st + lo.kd + T * 32 * kKdStride;
+      uint4 k[8];  // all reads issued before the first MFMA that needs them
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16(rp + 32 * ks);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        acc = mfma32(as_bf16x8(lds16(rp + 32 * ks)), half8(w.qv[ks >> 1], ks & 1), acc);
+        acc = mfma32(as_bf16x8(k[ks]), half8(w.qv[ks >> 1], ks & 1), acc);
     } else {
       const char *rp = st + lo.kn + T * 32 * kKnStride;
       const uint4 meta = lds16(st + lo.km + T * 32 * 16);
       const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
       if (kSmfmac) {
+        uint4 k[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) k[u] = lds16(rp + 32 * u);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          acc = smfmac32(as_bf16x8(lds16(rp + 32 * u)), w.qv[u], mw[u] >> (16 * hf), acc);
+          acc = smfmac32(as_bf16x8(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
       } else {
         // Decompress: the lane's 8-byte half of 16-byte unit ks (lo.kn carries +16 per half).
         const char *rq = rp - 8 * hf;
@@ -455,63 +461,91 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     while (kt <= kt_max && mode_k(kt) == 0) ++kt;
     return kt;
   };
-  // Direct loads of one tile into a stage. The per-lane global offsets are recomputed here (from
-  // an opaque copy of the lane index) rather than kept live across the loop.
-  auto issue = [&](int kt, int stage) {
+  // Per-lane global byte offsets of this wave's direct loads (load q = wave + 8 i of a region),
+  // computed once: [i] for the padded dense/2:4 rows, for both GEMM1 row orders of K (see tau).
+  uint32_t oKd[2][3], oKn[2][2], oKm[2], oVd[3], oVn[2], oVm;
+  {
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, sp); };
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int u = 64 * (wave + kWaves * i) + lane, row = u / 17, cu = u - 17 * row;
+        oKd[sp][i] = token(min(row, 63)) * 256 + 16 * min(cu, 15);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = 64 * (wave + kWaves * i) + lane, row = u / 9, cu = u - 9 * row;
+        oKn[sp][i] = token(min(row, 63)) * 128 + 16 * min(cu, 7);
+      }
+      oKm[sp] = token(lane) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int u = 64 * (wave + kWaves * i) + lane, ch = u / 9, cu = u - 9 * ch;
+      oVd[i] = min(ch, 127) * (2 * B) + 16 * min(cu, 7);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 64 * (wave + kWaves * i) + lane, ch = u / 5, cu = u - 5 * ch;
+      oVn[i] = min(ch, 127) * B + 16 * min(cu, 3);
+    }
+    const int d = 64 * ((wave + 5) & 3) + lane;  // block 128: waves 3..6 -> dword loads 0..3
+    oVm = B == 64 ? 16 * lane : (d >> 1) * (B / 8) + 4 * (d & 1);
+  }
+
+  // Direct loads of one tile (block modes mk, mv) into a stage.
+  auto issue = [&](int kt, int mk, int mv, int stage) {
     const int half = kt % TPB;
-    const int mk = mode_k(kt), mv = mode_v(kt);
     const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kKRegion;
-    const bool split = kSmfmac && mv > 0;  // GEMM1 row order of this tile (see tau)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, split); };
+    const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
     if (mk > 0) {
       const char *g = uniform_ptr(
           a.c.k_dense + ((size_t)(head * a.ndk + mk - 1) * B + kTile * half) * kD);
-      for (int q = wave; q < kKdUnits / 64; q += kWaves) {
-        const int u = 64 * q + ln, row = u / 17, cu = u - 17 * row;
-        dma16(g, token(row) * 256 + 16 * min(cu, 15), kl + 1024 * q);
-      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (wave + kWaves * i < kKdUnits / 64)
+          dma16(g, sp ? oKd[1][i] : oKd[0][i], kl + 1024 * (wave + kWaves * i));
     } else {
       const size_t row0 = (size_t)(head * a.nsk - mk - 1) * B + kTile * half;
       const char *g = uniform_ptr(a.c.k_nnz + row0 * (kD / 2));
-      for (int q = wave; q < kKnUnits / 64; q += kWaves) {
-        const int u = 64 * q + ln, row = u / 9, cu = u - 9 * row;
-        dma16(g, token(row) * 128 + 16 * min(cu, 7), kl + 1024 * q);
-      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (wave + kWaves * i < kKnUnits / 64)
+          dma16(g, sp ? oKn[1][i] : oKn[0][i], kl + 1024 * (wave + kWaves * i));
       if (wave == 1)
-        dma16(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), token(ln) * 16, kl + kKMetaOff);
+        dma16(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kKMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(a.c.v_dense + (size_t)(head * a.ndv + mv - 1) * B * kD +
                                   kTile * half);
-      for (int q = wave; q < kVdUnits / 64; q += kWaves) {
-        const int u = 64 * q + ln, ch = u / 9, cu = u - 9 * ch;
-        dma16(g, ch * (2 * B) + 16 * min(cu, 7), vl + 1024 * q);
-      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (wave + kWaves * i < kVdUnits / 64)
+          dma16(g, oVd[i], vl + 1024 * (wave + kWaves * i));
     } else {
       const size_t blk0 = (size_t)(head * a.nsv - mv - 1) * B * kD;
       const char *g = uniform_ptr(a.c.v_nnz + blk0 / 2 + (kTile / 2) * half);
-      for (int q = wave; q < kVnUnits / 64; q += kWaves) {
-        const int u = 64 * q + ln, ch = u / 5, cu = u - 5 * ch;
-        dma16(g, ch * B + 16 * min(cu, 3), vl + 1024 * q);
-      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (wave + kWaves * i < kVnUnits / 64)
+          dma16(g, oVn[i], vl + 1024 * (wave + kWaves * i));
       const char *gm = uniform_ptr(a.c.v_meta + blk0 / 16 + (kTile / 16) * half);
       if (B == 64) {
-        if (wave == 2) dma16(gm, 16 * ln, vl + kVMetaOff);
+        if (wave == 2) dma16(gm, oVm, vl + kVMetaOff);
       } else if (wave >= 3 && wave <= 6) {
-        const int d = 64 * (wave - 3) + ln;  // dword d: channel d/2, dword d%2 of its 8 bytes
-        dma4(gm, (d >> 1) * (B / 8) + 4 * (d & 1), vl + kVMetaOff + 256 * (wave - 3));
+        dma4(gm, oVm, vl + kVMetaOff + 256 * (wave - 3));
       }
     }
   };
-  auto count_of = [&](int kt) { return dma_count<B>(wave, mode_k(kt) > 0, mode_v(kt) > 0); };
-
   const float c = a.scale_log2;
+  // Tiles n, n+1, n+2 of the walk with their block modes (kt > kt_max: none).
   int kt0 = next_visible(0);
   int kt1 = kt0 <= kt_max ? next_visible(kt0 + 1) : kt_max + 1;
-  if (kt0 <= kt_max) issue(kt0, 0);
-  if (kt1 <= kt_max) issue(kt1, 1);
+  int mk0 = kt0 <= kt_max ? mode_k(kt0) : 0, mv0 = kt0 <= kt_max ? mode_v(kt0) : 0;
+  int mk1 = kt1 <= kt_max ? mode_k(kt1) : 0, mv1 = kt1 <= kt_max ? mode_v(kt1) : 0;
+  if (kt0 <= kt_max) issue(kt0, mk0, mv0, 0);
+  if (kt1 <= kt_max) issue(kt1, mk1, mv1, 1);
 
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
@@ -520,12 +554,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   int it = 0;
   while (kt0 <= kt_max) {
     const int kt2 = kt1 <= kt_max ? next_visible(kt1 + 1) : kt_max + 1;
-    wait_vmem(kt1 <= kt_max ? count_of(kt1) : 0);
+    const int mk2 = kt2 <= kt_max ? mode_k(kt2) : 0, mv2 = kt2 <= kt_max ? mode_v(kt2) : 0;
+    wait_vmem(kt1 <= kt_max ? dma_count<B>(wave, mk1 > 0, mv1 > 0) : 0);
     barrier();  // tile kt0 staged by every wave; stage (it + 2) % 4 no longer read
-    if (kt2 <= kt_max) issue(kt2, (it + 2) & 3);
+    if (kt2 <= kt_max) issue(kt2, mk2, mv2, (it + 2) & 3);
 
     const char *st = lds + (it & 3) * kStageBytes;
-    const bool sparse_k = mode_k(kt0) < 0, sparse_v = mode_v(kt0) < 0;
+    const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
       gemm1<true, kSmfmac>(w, st, lo, hf);
     else
@@ -537,7 +572,11 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     prev_sparse_v = sparse_v;
     st_prev = st;
     kt0 = kt1;
+    mk0 = mk1;
+    mv0 = mv1;
     kt1 = kt2;
+    mk1 = mk2;
+    mv1 = mv2;
     ++it;
   }
   // GEMM2 of the last tile (its stage is not overwritten after the loop).
