@@ -7,8 +7,10 @@ blocks -- the batch-8, 32K kernel benchmark setting of HieraSparse v2 §V-B1):
   hs_compress (score, rank, pack) of the 32K-token K/V cache,
   hs_prefill_attn causal over the 32K prompt (2:4 blocks on SMFMAC),
   hs_decode_attn of one new token per query head over the compressed cache.
-Each call is bracketed by HIP events on the stream the kernels run on. The same kernels on a cache
-compressed with every block dense give the same-kernel dense baseline.
+Each call is bracketed by HIP events on the stream the kernels run on. Between prefill and decode a
+read pass over 1 GiB (part of the step, outside both windows) settles the dirty cache lines of the
+prefill's 2 GiB output, so the decode window holds the decode's own HBM traffic. The same kernels
+on a cache compressed with every block dense give the same-kernel dense baseline.
 
 Output: one JSON line. value = decode HBM throughput (GB/s) on the compressed bytes the decode
 must read; roofline = the step's dominant kernel (prefill, matrix cores); the other kernels'
@@ -28,6 +30,7 @@ sys.path.insert(0, ROOT)
 WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
+SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
 
 
 def parse():
@@ -191,6 +194,12 @@ def main():
     o = torch.empty_like(q)
     lse_d = torch.empty((w.b, w.hq), device=dev, dtype=torch.float32)
 
+    # The prefill writes a 2 GiB output; the dirty lines it leaves in the last-level cache would be
+    # written back to HBM during whatever kernel runs next. A read pass over a buffer larger than
+    # that cache, between prefill and decode (inside the step, outside both kernels' windows),
+    # settles them, so the decode window measures the decode's own reads.
+    settle = torch.ones(SETTLE_BYTES // 4, device=dev, dtype=torch.int32)
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
@@ -200,14 +209,17 @@ def main():
         hs.hs_prefill_attn(shp, cnt, cache, Q, O, lse_p, 0.0, flags)
         if ev:
             ev[2].record(stream)
-        hs.hs_decode_attn(shp, cnt, cache, q, o, lse_d, 0.0, 0, ws_d)
+        settle.sum()
         if ev:
             ev[3].record(stream)
+        hs.hs_decode_attn(shp, cnt, cache, q, o, lse_d, 0.0, 0, ws_d)
+        if ev:
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -216,8 +228,8 @@ def main():
     wall = time.perf_counter() - t0
     comp_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     pre_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    dec_ms = np.array([e[3].elapsed_time(e[4]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in events])
 
     cache_bytes = hs.hs_cache_sizes(shp, cnt)
     map_k = cache["map_k"].cpu().numpy()
@@ -285,7 +297,7 @@ def main():
         hs.hs_compress(shp, cnt0, K, V, cache0, ws_c0)
         del ws_c0
         reps = max(3, args.steps // 2)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
         for r in range(reps + 1):
             e = ev[r - 1] if r else None
             if e:
@@ -293,12 +305,15 @@ def main():
             hs.hs_prefill_attn(shp, cnt0, cache0, Q, O, lse_p, 0.0, flags)
             if e:
                 e[1].record(stream)
-            hs.hs_decode_attn(shp, cnt0, cache0, q, o, lse_d, 0.0, 0, ws_d0)
+            settle.sum()
             if e:
                 e[2].record(stream)
+            hs.hs_decode_attn(shp, cnt0, cache0, q, o, lse_d, 0.0, 0, ws_d0)
+            if e:
+                e[3].record(stream)
         torch.cuda.synchronize()
         pre0 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
-        dec0 = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+        dec0 = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3
         w0 = w.with_counts(0, 0, 0)
         out["dense_baseline"] = {
             "decode_us": round(dec0 * 1e6, 2),

@@ -29,10 +29,11 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Per-source extra flags. The prefill kernel mixes dense MFMA and SMFMAC on the same accumulators;
-# SMFMAC's accumulator is always a VGPR tuple, so dense MFMAs there use the VGPR form as well (no
-# copies between accumulation and arch registers).
-EXTRA = {"hs_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags. The attention kernels mix dense MFMA and SMFMAC on the same
+# accumulators; SMFMAC's accumulator is always a VGPR tuple, so dense MFMAs there use the VGPR form
+# as well (no copies between accumulation and arch registers).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"hs_prefill.hip": _VGPR_FORM, "hs_decode.hip": _VGPR_FORM}
 
 
 def _compile(src, verbose):

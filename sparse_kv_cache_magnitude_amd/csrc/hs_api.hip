@@ -108,13 +108,14 @@ hs_status check_ptr(const void *p, const char *name, bool required = true) {
   return HS_OK;
 }
 
-// Split-KV factor of the decode: enough workgroups to cover the chip several times, with at
-// least four visible blocks per split.
+// Split-KV factor of the decode: the split kernel runs one wave per workgroup and two workgroups
+// per CU, so aim for 512 workgroups (two per CU on 256 CUs), with at least two visible blocks per
+// split.
 int auto_splits(const hs::Dims &d) {
-  const int heads = d.b * d.hkv;
+  const int units = d.b * d.hkv * ((d.G + 15) / 16);
   const int visible = d.nb - d.np;
-  int s = (2048 + heads - 1) / heads;
-  int cap = (visible + 3) / 4;
+  int s = (512 + units - 1) / units;
+  const int cap = (visible + 1) / 2;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   if (s > 512) s = 512;

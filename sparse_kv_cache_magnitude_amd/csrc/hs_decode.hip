@@ -3,17 +3,26 @@
 // "HieraSparse" (arXiv 2604.16864v2) §II Eq. (1), §III-C1 Table II "Trans-Both", §III-C2 mixed
 // dense / sparse dispatch, §IV-C split-KV decode + log-sum-exp combine + GQA packing.
 //
-// k_decode_split: one wave per (split, KV head, column group, batch entry). The query heads that
-//   share the KV head form the 16 columns of the matrix-core tiles ("a short duplicated sequence";
-//   unused columns are zero). The split walks its share of the head's visible blocks in 64-token
-//   tiles, streaming only the bytes of each block's representation straight into registers:
+// k_decode_split: one wave per workgroup, one workgroup per (split, KV head, column group, batch
+//   entry); two workgroups share a CU. The query heads that share the KV head form the 16 columns
+//   of the matrix-core tiles ("a short duplicated sequence"; unused columns are zero). A split owns
+//   a range of the head's visible blocks (balanced by visible blocks: pruned blocks cost nothing).
+//   The blocks' representations stream through two LDS stages by direct global->LDS loads
+//   (global_load_lds_dwordx4: whole 1 KB requests, no register staging), one 64-token tile ahead of
+//   the tile being computed:
 //     S^T = K Q^T   dense block: 16 v_mfma_f32_16x16x32_bf16; 2:4 block: 8 v_smfmac_f32_16x16x64_bf16
 //     online softmax per query column (exp2 domain), P^T packed to bf16 in place
 //     O^T += V^T P^T dense block: 16 MFMA over the channel-major copy; 2:4 block: 8 SMFMAC
-//   Pruned blocks are never touched. Splits are balanced by visible blocks, not raw block ranges.
 //   Output: per split, normalised partial o (fp32) and its log-sum-exp.
 // k_decode_combine: one workgroup per (batch entry, query head) merges the splits by their
 //   log-sum-exp and writes o (bf16) and lse.
+//
+// LDS tile layout (unpadded, 32 KB per stage): K rows are stored in the MFMA row order
+// (tile_token), V^T rows in channel order. The 16-byte units of every row are XOR-swizzled by a
+// function of the row, so that the 16 rows one operand read touches at one k-step land in distinct
+// bank groups. The swizzle of a row is the XOR of a per-lane part (the lane's position inside a
+// 1 KB load) and a per-load constant, so a load costs one precomputed lane offset plus uniform
+// arithmetic, and an operand read one precomputed lane offset plus an immediate.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -21,6 +30,14 @@ namespace hs {
 namespace {
 
 constexpr int kD = 128;
+constexpr int kTile = 64;
+constexpr int kKMeta = 8 * 1024;             // 2:4 K metadata inside the K region
+constexpr int kVReg = 16 * 1024;             // V region of a stage
+constexpr int kVMeta = 8 * 1024;             // 2:4 V metadata inside the V region
+constexpr int kStage = 32 * 1024;            // one tile: K 16 KB + V 16 KB (dense)
+constexpr int kListCap = 1024;               // visible blocks listed per pass
+constexpr int kListOff = 2 * kStage;         // map entries of the listed blocks (K, then V)
+constexpr int kLdsDec = kListOff + 2 * kListCap * 4;
 
 struct DecodeArgs {
   CacheView c;
@@ -30,14 +47,37 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// Row swizzles: 128-byte rows (8 units, 16 rows per operand read) and 64-byte rows (4 units).
+__device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int f4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// Direct loads one tile issues, by block modes (see issue() below).
+template <int B>
+__device__ __forceinline__ int tile_loads(int mk, int mv) {
+  return (mk > 0 ? 16 : 9) + (mv > 0 ? 16 : (B == 64 ? 9 : 12));
+}
+// Wait until at most n vector-memory operations are outstanding (n = a tile_loads value).
+__device__ __forceinline__ void wait_tile(int n) {
+  switch (n) {
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+    case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
+    case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
 template <int B>
 __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsDec];
   const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, hkv = a.hkv;
   const int h = blockIdx.y % hkv, cg = blockIdx.y / hkv, bi = blockIdx.z;
   const int head = bi * hkv + h;
   const int hq0 = h * a.G + 16 * cg, ncol = min(16, a.G - 16 * cg);
   const bool live = col < ncol;
+  constexpr int TPB = B / kTile;
 
   // Query registers: B operand of GEMM1, k-step s covers channels 32s .. 32s+31.
   uint4 qr[4];
@@ -48,100 +88,160 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       qr[s] = live ? *reinterpret_cast<const uint4 *>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
   }
 
-  // This split's visible blocks: ranks [lo, hi) among the head's non-pruned blocks.
-  const int lo = (int)((int64_t)split * a.nvis / a.splits);
-  const int hi = (int)((int64_t)(split + 1) * a.nvis / a.splits);
-  const int32_t *mkh = a.c.map_k + (size_t)head * a.nb;
-  const int32_t *mvh = a.c.map_v + (size_t)head * a.nb;
-  int j = a.nb;
-  {
-    int seen = 0;
-    for (int base = 0; base < a.nb && hi > lo; base += 64) {
-      const int jj = base + lane;
-      const bool vis = jj < a.nb && mkh[jj] != 0;
-      const uint64_t bal = __ballot(vis);
-      const int cnt = __popcll(bal);
-      if (seen + cnt > lo) {
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        const uint64_t hit = __ballot(vis && pre == lo - seen);
-        j = base + __ffsll((unsigned long long)hit) - 1;
-        break;
-      }
-      seen += cnt;
-    }
+  // ---- lane constants ----
+  // Operand reads (byte offsets inside a stage). GEMM1 reads row slot 16t + col (token
+  // tile_token(t, col)), GEMM2 reads channel 16ct + col.
+  int rk[4], rkn[2], rvd[2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) rk[s] = col * 256 + (((4 * s + g) ^ col) << 4);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    rkn[c2] = col * 128 + (((4 * c2 + g) ^ f8(col)) << 4);
+    rvd[c2] = kVReg + col * 128 + (((4 * c2 + g) ^ f8(col)) << 4);
   }
+  const int rkm = kKMeta + col * 16 + 2 * g;
+  const int rvn = kVReg + col * 64 + ((g ^ f4(col)) << 4);
+  const int rvm = kVReg + kVMeta + col * 8 + 2 * g;
+  // Direct loads (byte offsets from the global base of a load, before its uniform XOR part).
+  const int rr4 = lane >> 4, rr8 = lane >> 3, rr16 = lane >> 2;
+  const uint32_t dkd = rr4 * 256 + 16 * ((lane & 15) ^ rr4);
+  const uint32_t dkn = ((rr8 & 3) | ((rr8 & 4) << 1)) * 128 + 16 * ((lane & 7) ^ rr8);
+  const uint32_t dkm = (uint32_t)tile_token(lane >> 4, lane & 15) * 16;
+  const uint32_t dvd = rr8 * (2 * B) + 16 * ((lane & 7) ^ rr8);
+  const uint32_t dvn = rr16 * B + 16 * ((lane & 3) ^ f4(rr16));
+  const uint32_t dvm = B == 64 ? 16 * lane : (lane >> 1) * 16 + 4 * (lane & 1);
+
+  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
+  int32_t *lk = reinterpret_cast<int32_t *>(lds + kListOff), *lv = lk + kListCap;
+
+  // Direct loads of tile 'half' of a block (map entries mk, mv) into stage 'st'.
+  auto issue = [&](int mk, int mv, int half, int st) {
+    // Earlier reads of this stage are done, and at most 31 loads of the previous tile are still
+    // outstanding, so with this tile's (at most 32) the 6-bit load counter cannot overflow.
+    asm volatile("s_waitcnt vmcnt(31) lgkmcnt(0)" ::: "memory");
+    const uint32_t kl = lds_base + st * kStage, vl = kl + kVReg;
+    if (mk > 0) {
+      const char *gb = uniform_ptr(a.c.k_dense + ((size_t)(mk - 1) * B + kTile * half) * kD);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        // rows 4q .. 4q+3 of the MFMA row order are four consecutive tokens (one 1 KB chunk)
+        const int pq = ((q >> 2) & 1) | ((q & 3) << 1) | ((q >> 3) << 3);
+        dma16(gb + 1024 * pq, dkd ^ (64 * (q & 3)), kl + 1024 * q);
+      }
+    } else {
+      const size_t row0 = (size_t)(-mk - 1) * B + kTile * half;
+      const char *gb = uniform_ptr(a.c.k_nnz + row0 * (kD / 2));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // rows 8q .. 8q+7 are tokens tq + {0, 1, 2, 3, 8, 9, 10, 11}
+        const int tq = (((q >> 1) & 1) << 2) | ((q & 1) << 4) | ((q >> 2) << 5);
+        dma16(gb + 128 * tq, dkn ^ (16 * (q & 1)), kl + 1024 * q);
+      }
+      dma16(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), dkm, kl + kKMeta);
+    }
+    if (mv > 0) {
+      const char *gb = uniform_ptr(a.c.v_dense + (size_t)(mv - 1) * B * kD + kTile * half);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) dma16(gb + 16 * B * q, dvd ^ (16 * (q & 1)), vl + 1024 * q);
+    } else {
+      const size_t blk0 = (size_t)(-mv - 1) * B * kD;
+      const char *gb = uniform_ptr(a.c.v_nnz + blk0 / 2 + (kTile / 2) * half);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dma16(gb + 16 * B * q, dvn, vl + 1024 * q);
+      const char *gm = uniform_ptr(a.c.v_meta + blk0 / 16 + (kTile / 16) * half);
+      if (B == 64) {
+        dma16(gm, dvm, vl + kVMeta);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma4(gm + 512 * i, dvm, vl + kVMeta + 256 * i);
+      }
+    }
+  };
 
   f32x4 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int todo = hi - lo; todo > 0 && j < a.nb; ++j) {
-    const int mk = mkh[j];
-    if (mk == 0) continue;
-    --todo;
-    const int mv = mvh[j];
+  // This split's visible blocks: ranks [lo, hi) among the head's non-pruned blocks, listed in
+  // passes of at most kListCap blocks. 'seen' counts the visible blocks before block 'scan'.
+  const int lo = (int)((int64_t)split * a.nvis / a.splits);
+  const int hi = (int)((int64_t)(split + 1) * a.nvis / a.splits);
+  const int32_t *mkh = a.c.map_k + (size_t)head * a.nb;
+  const int32_t *mvh = a.c.map_v + (size_t)head * a.nb;
+  int scan = 0, seen = 0;
+  for (int rank = lo; rank < hi;) {
+    const int want = min(hi - rank, kListCap);
+    int got = 0;  // blocks listed in this pass
+    bool done = false;
+    while (!done) {
+      int mkv[4], mvv[4];
 #pragma unroll
-    for (int tile = 0; tile < B / 64; ++tile) {
-      // ---- issue this tile's K and V loads ----
-      uint4 ka[16], va[16];
-      uint32_t kix[8], vix[8];
-      if (mk > 0) {
-        const uint16_t *kb = a.c.k_dense + ((size_t)(mk - 1) * B + 64 * tile) * kD + 8 * g;
+      for (int i = 0; i < 4; ++i) {
+        const int j = scan + 64 * i + lane;
+        mkv[i] = j < a.nb ? mkh[j] : 0;
+        mvv[i] = j < a.nb ? mvh[j] : 0;
+      }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            ka[4 * t + s] =
-                *reinterpret_cast<const uint4 *>(kb + (size_t)tile_token(t, col) * kD + 32 * s);
-      } else {
-        const size_t sb = (size_t)(-mk - 1) * B + 64 * tile;
-        const uint16_t *nb_ = a.c.k_nnz + sb * (kD / 2) + 8 * g;
-        const uint16_t *mb = a.c.k_meta + sb * (kD / 16) + g;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int tok = tile_token(t, col);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            ka[2 * t + c] = *reinterpret_cast<const uint4 *>(nb_ + (size_t)tok * (kD / 2) + 32 * c);
-            kix[2 * t + c] = mb[(size_t)tok * (kD / 16) + 4 * c];
-          }
+      for (int i = 0; i < 4; ++i) {
+        if (done) break;
+        const uint64_t bal = __ballot(mkv[i] != 0);
+        const int r = seen + __popcll(bal & ((1ull << lane) - 1ull)) - rank;
+        if (mkv[i] != 0 && r >= 0 && r < want) {
+          lk[r] = mkv[i];
+          lv[r] = mvv[i];
+        }
+        const int cnt = __popcll(bal);
+        got = min(seen + cnt - rank, want);
+        if (seen + cnt > rank + want) {
+          done = true;  // the next pass lists the rest of this chunk
+        } else {
+          seen += cnt;
+          scan += 64;
+          done = seen == rank + want || scan >= a.nb;
         }
       }
-      if (mv > 0) {
-        const uint16_t *vb = a.c.v_dense + (size_t)(mv - 1) * B * kD + 64 * tile + 8 * g;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            va[2 * ct + m] =
-                *reinterpret_cast<const uint4 *>(vb + (size_t)(16 * ct + col) * B + 32 * m);
+    }
+    if (got <= 0) break;  // the map holds fewer visible blocks than the counts say
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+    const int ntiles = got * TPB;
+    auto mk_of = [&](int n) { return __builtin_amdgcn_readfirstlane(lk[n / TPB]); };
+    auto mv_of = [&](int n) { return __builtin_amdgcn_readfirstlane(lv[n / TPB]); };
+    int mk0 = mk_of(0), mv0 = mv_of(0);
+    issue(mk0, mv0, 0, 0);
+    for (int n = 0; n < ntiles; ++n) {
+      int mk1 = 0, mv1 = 0;
+      if (n + 1 < ntiles) {
+        mk1 = mk_of(n + 1);
+        mv1 = mv_of(n + 1);
+        issue(mk1, mv1, (n + 1) % TPB, (n + 1) & 1);
+        wait_tile(tile_loads<B>(mk1, mv1));
       } else {
-        const size_t sb = (size_t)(-mv - 1) * B * kD;
-        const uint16_t *nb_ = a.c.v_nnz + sb / 2 + 32 * tile + 8 * g;
-        const uint16_t *mb = a.c.v_meta + sb / 16 + 4 * tile + g;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          va[ct] = *reinterpret_cast<const uint4 *>(nb_ + (size_t)(16 * ct + col) * (B / 2));
-          vix[ct] = mb[(size_t)(16 * ct + col) * (B / 16)];
-        }
+        wait_tile(0);
       }
+      const char *kl = lds + (n & 1) * kStage;
 
       // ---- S^T = K Q^T ----
       f32x4 sacc[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (mk > 0) {
+      if (mk0 > 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sacc[t] = mfma16(ka[4 * t + s], qr[s], sacc[t]);
+          for (int s = 0; s < 4; ++s)
+            sacc[t] = mfma16(*reinterpret_cast<const uint4 *>(kl + rk[s] + 4096 * t), qr[s],
+                             sacc[t]);
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            sacc[t] = smfmac16(ka[2 * t + c], qr[2 * c], qr[2 * c + 1], kix[2 * t + c], sacc[t]);
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const uint4 kv = *reinterpret_cast<const uint4 *>(kl + rkn[c2] + 2048 * t);
+            const uint32_t ix = *reinterpret_cast<const uint16_t *>(kl + rkm + 256 * t + 8 * c2);
+            sacc[t] = smfmac16(kv, qr[2 * c2], qr[2 * c2 + 1], ix, sacc[t]);
+          }
       }
 
       // ---- online softmax over this tile's 64 tokens, per query column ----
@@ -156,14 +256,16 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       float psum = 0.f;
       uint32_t pp[8];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float p0 = exp2f(sacc[t][0] - m_new), p1 = exp2f(sacc[t][1] - m_new);
-        float p2 = exp2f(sacc[t][2] - m_new), p3 = exp2f(sacc[t][3] - m_new);
+        const float p0 = __builtin_amdgcn_exp2f(sacc[t][0] - m_new);
+        const float p1 = __builtin_amdgcn_exp2f(sacc[t][1] - m_new);
+        const float p2 = __builtin_amdgcn_exp2f(sacc[t][2] - m_new);
+        const float p3 = __builtin_amdgcn_exp2f(sacc[t][3] - m_new);
         psum += (p0 + p1) + (p2 + p3);
         pp[2 * t] = pack_bf16x2(p0, p1);
         pp[2 * t + 1] = pack_bf16x2(p2, p3);
@@ -175,17 +277,26 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       const uint4 phi = make_uint4(pp[4], pp[5], pp[6], pp[7]);  // tokens 32+8g .. 32+8g+7
 
       // ---- O^T += V^T P^T ----
-      if (mv > 0) {
+      if (mv0 > 0) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-          oacc[ct] = mfma16(va[2 * ct], plo, oacc[ct]);
-          oacc[ct] = mfma16(va[2 * ct + 1], phi, oacc[ct]);
+          oacc[ct] = mfma16(*reinterpret_cast<const uint4 *>(kl + rvd[0] + 2048 * ct), plo,
+                            oacc[ct]);
+          oacc[ct] = mfma16(*reinterpret_cast<const uint4 *>(kl + rvd[1] + 2048 * ct), phi,
+                            oacc[ct]);
         }
       } else {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) oacc[ct] = smfmac16(va[ct], plo, phi, vix[ct], oacc[ct]);
+        for (int ct = 0; ct < 8; ++ct) {
+          const uint4 vv = *reinterpret_cast<const uint4 *>(kl + rvn + 1024 * ct);
+          const uint32_t ix = *reinterpret_cast<const uint16_t *>(kl + rvm + 128 * ct);
+          oacc[ct] = smfmac16(vv, plo, phi, ix, oacc[ct]);
+        }
       }
+      mk0 = mk1;
+      mv0 = mv1;
     }
+    rank += got;
   }
 
   // ---- normalised partial output and log-sum-exp of this split ----

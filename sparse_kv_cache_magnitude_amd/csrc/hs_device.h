@@ -127,6 +127,56 @@ __device__ __forceinline__ int tile_token(int t, int r) {
 }
 
 // ----------------------------------------------------------------------------------------------
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4 / _dword).
+// Lane i of the wave writes LDS[lds_addr + size * i]; the global address is gbase + voff (per lane).
+// Issued through inline assembly so the compiler does not serialise them with its own wait
+// insertion; completion is tracked with explicit vmcnt waits before the per-tile barrier.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+// Wait until at most n of this wave's vector-memory operations are outstanding (n in 0..6).
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ const char *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char *)(((uint64_t)hi << 32) | lo);
+}
+
+// ----------------------------------------------------------------------------------------------
 // Wave helpers.
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
