@@ -122,9 +122,16 @@ int auto_splits(const hs::Dims &d) {
   return s;
 }
 
+// Decode workspace: the split counters (one uint32 per batch entry, KV head and group of 16 query
+// heads, padded to 256 bytes; zero between calls), then the fp32 partial outputs and log-sum-exps.
+size_t decode_counter_bytes(const hs::Dims &d) {
+  const size_t n = (size_t)d.b * d.hkv * ((d.G + 15) / 16) * sizeof(uint32_t);
+  return (n + 255) / 256 * 256;
+}
+
 size_t decode_ws_bytes(const hs::Dims &d, int splits) {
   const size_t rows = (size_t)d.b * d.hq * splits;
-  return rows * d.D * sizeof(float) + rows * sizeof(float);
+  return decode_counter_bytes(d) + rows * d.D * sizeof(float) + rows * sizeof(float);
 }
 
 size_t compress_ws_bytes(const hs::Dims &d) { return (size_t)d.b * d.hkv * d.nb * 3 * sizeof(uint64_t); }
@@ -201,10 +208,11 @@ HS_API hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts,
     return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
                 ws ? "" : ", NULL");
   if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
-  float *part_o = (float *)ws;
+  uint32_t *counters = (uint32_t *)ws;
+  float *part_o = (float *)((char *)ws + decode_counter_bytes(d));
   float *part_lse = part_o + (size_t)d.b * d.hq * splits * d.D;
   hipError_t e = hs::launch_decode(d, c, q, o, lse, scale_log2(softmax_scale, d.D), splits, part_o,
-                                   part_lse, (hipStream_t)stream);
+                                   part_lse, counters, (hipStream_t)stream);
   if (e != hipSuccess) return fail(HS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }

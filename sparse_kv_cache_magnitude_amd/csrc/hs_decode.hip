@@ -6,16 +6,16 @@
 // k_decode_split: one wave per workgroup, one workgroup per (split, KV head, column group, batch
 //   entry); two workgroups share a CU. The query heads that share the KV head form the 16 columns
 //   of the matrix-core tiles ("a short duplicated sequence"; unused columns are zero). A split owns
-//   a range of the head's visible blocks (balanced by visible blocks: pruned blocks cost nothing).
+//   a run of the head's visible blocks, balanced by bytes (pruned blocks cost nothing).
 //   The blocks' representations stream through two LDS stages by direct global->LDS loads
 //   (global_load_lds_dwordx4: whole 1 KB requests, no register staging), one 64-token tile ahead of
 //   the tile being computed:
 //     S^T = K Q^T   dense block: 16 v_mfma_f32_16x16x32_bf16; 2:4 block: 8 v_smfmac_f32_16x16x64_bf16
 //     online softmax per query column (exp2 domain), P^T packed to bf16 in place
 //     O^T += V^T P^T dense block: 16 MFMA over the channel-major copy; 2:4 block: 8 SMFMAC
-//   Output: per split, normalised partial o (fp32) and its log-sum-exp.
-// k_decode_combine: one workgroup per (batch entry, query head) merges the splits by their
-//   log-sum-exp and writes o (bf16) and lse.
+//   Every split writes its normalised partial o (fp32) and log-sum-exp to the workspace; the last
+//   split of each (batch entry, KV head, column group) to finish, picked by an atomic ticket,
+//   merges the splits by their log-sum-exp and writes o (bf16) and lse.
 //
 // LDS tile layout (unpadded, 32 KB per stage): K rows are stored in the MFMA row order
 // (tile_token), V^T rows in channel order. The 16-byte units of every row are XOR-swizzled by a
@@ -42,10 +42,19 @@ constexpr int kLdsDec = kListOff + 2 * kListCap * 4;
 struct DecodeArgs {
   CacheView c;
   const uint16_t *q;
+  uint16_t *o;
+  float *lse;
   float *part_o, *part_lse;
-  int nb, nvis, hkv, hq, G, splits;
+  uint32_t *counters;
+  int nb, total_w, hkv, hq, G, splits;
   float scale_log2;
 };
+
+// Device-scope (coherent across the XCDs' L2 caches) relaxed store of a float.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Row swizzles: 128-byte rows (8 units, 16 rows per operand read) and 64-byte rows (4 units).
 __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -65,6 +74,87 @@ __device__ __forceinline__ void wait_tile(int n) {
     case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
     case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Merge the splits of ncol query heads (partial rows row0 + c * splits + s; output rows orow0 + c)
+// by their log-sum-exps: o = sum_s e^(lse_s - m) o_s / sum_s e^(lse_s - m), lse = m + log(sum).
+// Lane l owns channels 4 (l % 32) .. +3 and the splits of parity l / 32, four query heads at a
+// time. Padding entries (heads past ncol, splits past the end) read a valid row with weight 0, so
+// every load is unconditional and one round of loads covers four heads.
+__device__ __forceinline__ void combine(const DecodeArgs &a, size_t row0, size_t orow0, int ncol,
+                                        int lane) {
+  const int S = a.splits, q4 = lane & 31, hh = lane >> 5;
+  for (int c0 = 0; c0 < ncol; c0 += 4) {
+    const float *pl[4];
+    const float *pc[4];
+    float mx[4], wsum[4];
+    f32x4 acc[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const size_t r = row0 + (size_t)min(c0 + cc, ncol - 1) * S;
+      pl[cc] = a.part_lse + r;
+      pc[cc] = a.part_o + r * kD + 4 * q4;
+      mx[cc] = -INFINITY;
+      wsum[cc] = 0.f;
+      acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float ls0[4];  // log-sum-exps of splits 0 .. 63, kept for the weights below
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) mx[cc] = ls0[cc] = pl[cc][min(lane, S - 1)];
+    for (int s0 = 64; s0 < S; s0 += 64) {
+      const int sl = min(s0 + lane, S - 1);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) mx[cc] = fmaxf(mx[cc], pl[cc][sl]);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx[cc] = fmaxf(mx[cc], __shfl_xor(mx[cc], o, 64));
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int ns = min(64, S - s0), sl = min(lane, ns - 1);
+      float wl[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const float ls = s0 == 0 ? ls0[cc] : pl[cc][s0 + sl];
+        const bool use = c0 + cc < ncol && lane < ns && ls != -INFINITY;
+        wl[cc] = use ? __expf(ls - mx[cc]) : 0.f;
+      }
+      for (int k0 = 0; 2 * k0 < ns; k0 += 4) {  // 8 splits (4 per lane half) per round
+        float4 v[4][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const int sp = min(2 * (k0 + kk) + hh, ns - 1);  // past the end: weight 0 below
+            v[kk][cc] = *reinterpret_cast<const float4 *>(pc[cc] + (size_t)(s0 + sp) * kD);
+          }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const int sr = 2 * (k0 + kk) + hh;
+            const float w = __shfl(wl[cc], min(sr, ns - 1), 64) * (sr < ns ? 1.f : 0.f);
+            wsum[cc] += w;
+            acc[cc] += w * f32x4{v[kk][cc].x, v[kk][cc].y, v[kk][cc].z, v[kk][cc].w};
+          }
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      wsum[cc] += __shfl_xor(wsum[cc], 32, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[cc][i] += __shfl_xor(acc[cc][i], 32, 64);
+      if (c0 + cc >= ncol) continue;
+      const float inv = wsum[cc] > 0.f ? 1.f / wsum[cc] : 0.f;
+      const size_t orow = orow0 + c0 + cc;
+      if (hh == 0)
+        *reinterpret_cast<uint2 *>(a.o + orow * kD + 4 * q4) =
+            make_uint2(pack_bf16x2(acc[cc][0] * inv, acc[cc][1] * inv),
+                       pack_bf16x2(acc[cc][2] * inv, acc[cc][3] * inv));
+      if (a.lse && lane == 0)
+        a.lse[orow] = wsum[cc] > 0.f ? mx[cc] + __logf(wsum[cc]) : -INFINITY;
+    }
   }
 }
 
@@ -163,18 +253,22 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // This split's visible blocks: ranks [lo, hi) among the head's non-pruned blocks, listed in
-  // passes of at most kListCap blocks. 'seen' counts the visible blocks before block 'scan'.
-  const int lo = (int)((int64_t)split * a.nvis / a.splits);
-  const int hi = (int)((int64_t)(split + 1) * a.nvis / a.splits);
+  // This split's blocks. Splits are balanced by the loads their blocks issue (i.e. by bytes): with
+  // w_j the load count of visible block j, p_j the sum of w over the blocks before it and W the sum
+  // over the head, block j belongs to split floor((2 p_j + w_j) S / 2W) -- the split whose share of
+  // W holds the block's midpoint (clamped to the last split). The blocks are listed in LDS a batch
+  // of four 64-block chunks at a time, in passes of at most kListCap entries.
   const int32_t *mkh = a.c.map_k + (size_t)head * a.nb;
   const int32_t *mvh = a.c.map_v + (size_t)head * a.nb;
-  int scan = 0, seen = 0;
-  for (int rank = lo; rank < hi;) {
-    const int want = min(hi - rank, kListCap);
+  const int64_t two_w = 2 * (int64_t)a.total_w;
+  const int64_t lo_key = two_w * split, hi_key = two_w * (split + 1);
+  const bool last_split = split == a.splits - 1;
+  int scan = 0;       // first block of the next chunk
+  int64_t base = 0;   // sum of w over the blocks before 'scan'
+  bool finished = a.total_w <= 0;
+  while (!finished) {
     int got = 0;  // blocks listed in this pass
-    bool done = false;
-    while (!done) {
+    while (!finished && got <= kListCap - 256) {
       int mkv[4], mvv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -184,25 +278,31 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (done) break;
-        const uint64_t bal = __ballot(mkv[i] != 0);
-        const int r = seen + __popcll(bal & ((1ull << lane) - 1ull)) - rank;
-        if (mkv[i] != 0 && r >= 0 && r < want) {
+        if (finished) break;
+        const int w = mkv[i] != 0 ? TPB * tile_loads<B>(mkv[i], mvv[i]) : 0;
+        int incl = w;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        const int64_t key = (2 * (base + incl - w) + w) * (int64_t)a.splits;
+        const bool mine = w > 0 && key >= lo_key && (key < hi_key || last_split);
+        const uint64_t bal = __ballot(mine);
+        if (mine) {
+          const int r = got + __popcll(bal & ((1ull << lane) - 1ull));
           lk[r] = mkv[i];
           lv[r] = mvv[i];
         }
-        const int cnt = __popcll(bal);
-        got = min(seen + cnt - rank, want);
-        if (seen + cnt > rank + want) {
-          done = true;  // the next pass lists the rest of this chunk
-        } else {
-          seen += cnt;
-          scan += 64;
-          done = seen == rank + want || scan >= a.nb;
-        }
+        got += __popcll(bal);
+        base += __shfl(incl, 63, 64);
+        scan += 64;
+        // keys grow with the block index: once one passes this split's share, the rest do too
+        const bool past = !last_split && __ballot(w > 0 && key >= hi_key) != 0;
+        finished = past || scan >= a.nb;
       }
     }
-    if (got <= 0) break;  // the map holds fewer visible blocks than the counts say
+    if (got == 0) break;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     const int ntiles = got * TPB;
@@ -296,60 +396,57 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       mk0 = mk1;
       mv0 = mv1;
     }
-    rank += got;
   }
 
   // ---- normalised partial output and log-sum-exp of this split ----
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!live) return;
-  const size_t row = ((size_t)bi * a.hq + hq0 + col) * a.splits + split;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float *po = a.part_o + row * kD + 4 * g;
+  const size_t row0 = ((size_t)bi * a.hq + hq0) * a.splits;  // partial row of column 0, split 0
+  if (live) {
+    const size_t row = row0 + (size_t)col * a.splits + split;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float *po = a.part_o + row * kD + 4 * g;
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-    *reinterpret_cast<float4 *>(po + 16 * ct) =
-        make_float4(oacc[ct][0] * inv, oacc[ct][1] * inv, oacc[ct][2] * inv, oacc[ct][3] * inv);
-  if (g == 0) a.part_lse[row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-}
-
-__global__ __launch_bounds__(128) void k_decode_combine(const float *__restrict__ part_o,
-                                                        const float *__restrict__ part_lse,
-                                                        int splits, uint16_t *__restrict__ o,
-                                                        float *__restrict__ lse) {
-  const size_t row = blockIdx.x;
-  const int d = threadIdx.x;
-  const float *pl = part_lse + row * splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pl[s]);
-  float acc = 0.f, wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float w = pl[s] == -INFINITY ? 0.f : __expf(pl[s] - mx);
-      wsum += w;
-      acc += w * part_o[(row * splits + s) * kD + d];
-    }
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_coherent(po + 16 * ct + i, oacc[ct][i] * inv);
+    if (g == 0)
+      store_coherent(a.part_lse + row, l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY);
   }
-  const float out = wsum > 0.f ? acc / wsum : 0.f;
-  o[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)out);
-  if (lse && d == 0) lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+
+  // ---- log-sum-exp combine, §IV-C: the last split of this (batch entry, KV head, column group)
+  // to finish, picked by an atomic ticket, merges all splits; no workgroup waits for another.
+  // The partials were written through to the device coherence point (device-scope stores, which
+  // leave no dirty lines in the per-XCD L2) and have completed before the ticket is taken; the
+  // merging split invalidates its caches (device-scope acquire) before it reads them.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t *ctr = a.counters + (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  uint32_t ticket = 0;
+  if (lane == 0)
+    ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ticket = __shfl(ticket, 0, 64);
+  if (ticket != (uint32_t)(a.splits - 1)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  combine(a, row0, (size_t)bi * a.hq + hq0, ncol, lane);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                          float *lse, float scale_log2, int splits, float *part_o, float *part_lse,
-                         hipStream_t stream) {
-  DecodeArgs a{c, q, part_o, part_lse, d.nb, d.nb - d.np, d.hkv, d.hq, d.G, splits, scale_log2};
+                         uint32_t *counters, hipStream_t stream) {
+  // Loads of one head's visible blocks (the per-tile counts of tile_loads, times tiles per block).
+  const int total_w =
+      (d.B / kTile) * (d.ndk * 16 + d.nsk * 9 + d.ndv * 16 + d.nsv * (d.B == 64 ? 9 : 12));
+  DecodeArgs a{c, q, o, lse, part_o, part_lse, counters, d.nb, total_w, d.hkv, d.hq, d.G, splits,
+               scale_log2};
   const int col_groups = (d.G + 15) / 16;
   const dim3 grid(splits, d.hkv * col_groups, d.b);
   if (d.B == 64)
     k_decode_split<64><<<grid, 64, 0, stream>>>(a);
   else
     k_decode_split<128><<<grid, 64, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_decode_combine<<<d.b * d.hq, 128, 0, stream>>>(part_o, part_lse, splits, o, lse);
   return hipGetLastError();
 }
 

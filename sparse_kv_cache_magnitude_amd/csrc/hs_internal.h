@@ -24,9 +24,11 @@ struct CacheView {
 hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
                            uint64_t *keys, hipStream_t stream);
 
+// counters: one uint32 per (batch entry, KV head, column group of 16 query heads), zero before
+// the call and zero again after it.
 hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                          float *lse, float scale_log2, int splits, float *part_o, float *part_lse,
-                         hipStream_t stream);
+                         uint32_t *counters, hipStream_t stream);
 
 hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                           float *lse, float scale_log2, bool smfmac, hipStream_t stream);

@@ -136,3 +136,29 @@ def test_decode_deterministic():
     o1, l1, cache = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q)
     o2, l2, _ = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q, cache=cache)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_workspace_reuse():
+    """One zero-filled workspace serves calls of different shapes and split counts in a row: the
+    split counters at its start are zero again after every call, and every output is correct."""
+    rng = np.random.default_rng(21)
+    cases = [(2, 40, 2, 64 * 11, 64, (2, 5, 3), 7),    # G = 20: two column groups per KV head
+             (1, 8, 2, 128 * 9, 128, (1, 4, 4), 3),
+             (2, 40, 2, 64 * 11, 64, (2, 5, 3), 0)]
+    shapes = [(hs.shape(b, hq, hkv, L, 128, B), hs.counts(*c), s) for b, hq, hkv, L, B, c, s in cases]
+    n = max(hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) for shp, cnt, s in shapes)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    groups = max(b * hkv * ((hq // hkv + 15) // 16) for b, hq, hkv, *_ in cases)
+    for (b, hq, hkv, L, B, counts, splits), (shp, cnt, _) in zip(cases, shapes):
+        K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+        V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+        q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
+        cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+        o = torch.empty((b, hq, 128), dtype=torch.int16, device="cuda")
+        lse = torch.empty((b, hq), dtype=torch.float32, device="cuda")
+        hs.hs_decode_attn(shp, cnt, cache, gu.to_dev(q), o, lse, 0.0, splits, ws)
+        torch.cuda.synchronize()
+        assert (ws[:4 * groups] == 0).all(), "split counters not reset"
+        ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
+        assert_close(synth.bf16_to_f32(gu.to_host_u16(o)), ref, lse.cpu().numpy(), ref_lse,
+                     f"reuse b={b} hq={hq} B={B} splits={splits}")
