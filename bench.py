@@ -31,6 +31,15 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
+COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
+COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
+
+# Kernels whose HBM traffic is summarised, with the sources their digest covers.
+TRAFFIC_KERNELS = {"k_prefill": ("hs_prefill.hip", "hs_device.h"),
+                   "k_decode_split": ("hs_decode.hip", "hs_device.h"),
+                   "k_score": ("hs_compress.hip", "hs_device.h"),
+                   "k_rank": ("hs_compress.hip", "hs_device.h"),
+                   "k_pack": ("hs_compress.hip", "hs_device.h")}
 
 
 def parse():
@@ -43,6 +52,12 @@ def parse():
     p.add_argument("--no-dense-baseline", action="store_true")
     p.add_argument("--cpu-sample-heads", type=int, default=16,
                    help="(batch, KV head) pairs the oracle runs for the CPU baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="first run a plain device copy of COPY_BYTES (reads and writes a known "
+                        "number of bytes: the calibration of rocprofv3's byte counters)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                        "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -107,6 +122,59 @@ def measured_traffic(kernel_key, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
+def summarize_counters(fetch_dir, write_dir):
+    """HBM bytes per launch of the hot-path kernels from two rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch). Each counter is scaled by the bytes the calibration copy really
+    moves over what the same counter reads for it. Writes profiles/traffic.json."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def per_kernel(d, counter):
+        paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = defaultdict(lambda: defaultdict(float))
+        for path in paths:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        out = {}
+        for name, per_dispatch in vals.items():
+            key = next((k for k in list(TRAFFIC_KERNELS) + [COPY_KERNEL] if k in name), None)
+            if key:
+                v = list(per_dispatch.values())
+                prev = out.get(key, [])
+                out[key] = prev + v
+        return out
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    if COPY_KERNEL not in fetch or COPY_KERNEL not in write:
+        raise SystemExit("the calibration copy is missing: run the profiled command with "
+                         "--copy-probe")
+    kib = lambda xs: sum(xs) / len(xs)
+    f_scale = COPY_BYTES / (kib(fetch[COPY_KERNEL]) * 1024)
+    w_scale = COPY_BYTES / (kib(write[COPY_KERNEL]) * 1024)
+    rec = {"calibration": {"kernel": COPY_KERNEL, "bytes_read": COPY_BYTES,
+                           "bytes_written": COPY_BYTES,
+                           "fetch_kib": round(kib(fetch[COPY_KERNEL]), 1),
+                           "write_kib": round(kib(write[COPY_KERNEL]), 1),
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
+    for k, srcs in TRAFFIC_KERNELS.items():
+        if k in fetch and k in write:
+            fb, wb = kib(fetch[k]) * 1024 * f_scale, kib(write[k]) * 1024 * w_scale
+            rec[k] = {"source_digest": source_digest(*srcs), "dispatches": len(fetch[k]),
+                      "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                      "hbm_bytes_per_launch": round(fb + wb)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
 # ------------------------------------------------------------------------------------------------
 
 def make_inputs(w, torch, dev):
@@ -166,6 +234,8 @@ def cpu_baseline(w, heads, min_seconds=10.0):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -182,6 +252,14 @@ def main():
     dev = "cuda"
     stream = torch.cuda.current_stream()
     flags = hs.HS_PREFILL_SMFMAC if args.prefill_path == "smfmac" else hs.HS_PREFILL_DECOMPRESS
+
+    if args.copy_probe:
+        src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     K, V, Q, q = make_inputs(w, torch, dev)
     shp = hs.shape(w.b, w.hq, w.hkv, w.L, w.D, w.B)
@@ -277,7 +355,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre_exec_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("k_prefill", source_digest(
                          "hs_prefill.hip", "hs_device.h"))},
-        "roofline_decode": {"bound": "hbm", "kernel": "k_decode_split+k_decode_combine",
+        "roofline_decode": {"bound": "hbm", "kernel": "k_decode_split",
                             "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("k_decode_split", source_digest(
