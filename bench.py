@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="first run a plain device copy of COPY_BYTES (reads and writes a known "
                         "number of bytes: the calibration of rocprofv3's byte counters)")
+    p.add_argument("--suite", action="store_true",
+                   help="instead of the headline step: one JSON line per further workload (16K "
+                        "prefill with both 2:4 paths, 128K decode, the sparsity sweeps)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -232,10 +235,137 @@ def cpu_baseline(w, heads, min_seconds=10.0):
             "decode_s_per_rep": round(per, 4), "compress_s": round(t1 - t0, 3)}
 
 
+def run_suite(reps=7):
+    """The further measured workloads, one JSON line each: the 16K causal prefill with 128-token
+    blocks on both 2:4 paths, the 128K long-context decode, and the sparsity sweeps (decode and
+    compressor at 64K / batch 16, prefill at 32K / batch 1). Every timing is the median of `reps`
+    HIP-event windows around one call; each decode window follows a 1 GiB read pass (the settled,
+    cold-cache state). Each workload is also run on an all-dense cache (same kernels)."""
+    import numpy as np
+    import torch
+    from sparse_kv_cache_magnitude_amd import hierasparse as hs
+    from sparse_kv_cache_magnitude_amd import synth
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    settle = torch.ones(SETTLE_BYTES // 4, device=dev, dtype=torch.float32)
+
+    def timed(fn, pre=None):
+        ts = []
+        for _ in range(reps + 1):
+            if pre:
+                pre()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return float(np.median(ts[1:]))
+
+    def setup(w, counts=None):
+        K, V, Q, q = make_inputs(w, torch, dev)
+        shp = hs.shape(w.b, w.hq, w.hkv, w.L, w.D, w.B)
+        cnt = hs.counts(*(counts or (w.n_p, w.n_sk, w.n_sv)))
+        cache = hs.alloc_cache(shp, cnt)
+        ws_c = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+        comp = timed(lambda: hs.hs_compress(shp, cnt, K, V, cache, ws_c))
+        return K, V, Q, q, shp, cnt, cache, comp
+
+    def decode_time(shp, cnt, cache, q):
+        ws = hs.alloc_workspace(hs.HS_OP_DECODE, shp, cnt)
+        o = torch.empty_like(q)
+        return timed(lambda: hs.hs_decode_attn(shp, cnt, cache, q, o, None, 0.0, 0, ws),
+                     pre=lambda: settle.sum())
+
+    def prefill_time(shp, cnt, cache, Q, flags):
+        O = torch.empty_like(Q)
+        return timed(lambda: hs.hs_prefill_attn(shp, cnt, cache, Q, O, None, 0.0, flags))
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    # ---- 16K causal prefill, 128-token blocks, both 2:4 paths ----
+    w = synth.workload("prefill_16k_b1_B128")
+    K, V, Q, q, shp, cnt, cache, comp = setup(w)
+    mk, mv = cache["map_k"].cpu().numpy(), cache["map_v"].cpu().numpy()
+    t_s = prefill_time(shp, cnt, cache, Q, hs.HS_PREFILL_SMFMAC)
+    t_d = prefill_time(shp, cnt, cache, Q, hs.HS_PREFILL_DECOMPRESS)
+    dense_eq, ex_s, full = prefill_flops(w, mk, mv, True)
+    _, ex_d, _ = prefill_flops(w, mk, mv, False)
+    _, _, _, _, shp0, cnt0, cache0, _ = setup(w, (0, 0, 0))
+    t0 = prefill_time(shp0, cnt0, cache0, Q, hs.HS_PREFILL_SMFMAC)
+    peak = BF16_DENSE_PEAK_TFLOPS * 1e12
+    emit({"suite": w.name, "prefill_ms_smfmac": round(t_s * 1e3, 3),
+          "prefill_ms_decompress": round(t_d * 1e3, 3), "prefill_ms_dense_cache": round(t0 * 1e3, 3),
+          "tflops_dense_equivalent_smfmac": round(dense_eq / t_s / 1e12, 1),
+          "mfma_utilisation_smfmac": round(ex_s / peak / t_s, 4),
+          "mfma_utilisation_decompress": round(ex_d / peak / t_d, 4),
+          "mfma_utilisation_dense_cache": round(full / peak / t0, 4),
+          "speedup_vs_dense_smfmac": round(t0 / t_s, 3),
+          "speedup_vs_dense_decompress": round(t0 / t_d, 3),
+          "smfmac_over_decompress_speed": round(t_d / t_s, 3),
+          "ideal_speedup_executed_flops": round(full / ex_s, 3),
+          "compress_us": round(comp * 1e6, 1), "compress_share_of_prefill": round(comp / t_s, 5)})
+    del K, V, Q, q, cache, cache0
+
+    # ---- 128K long-context decode ----
+    w = synth.workload("decode_128k_b4")
+    G = w.hq // w.hkv
+    K, V, Q, q, shp, cnt, cache, comp = setup(w)
+    del Q
+    t = decode_time(shp, cnt, cache, q)
+    _, _, _, _, shp0, cnt0, cache0, _ = setup(w, (0, 0, 0))
+    t0 = decode_time(shp0, cnt0, cache0, q)
+    nbytes, nbytes0 = decode_bytes(w, G), decode_bytes(w.with_counts(0, 0, 0), G)
+    emit({"suite": w.name, "decode_us": round(t * 1e6, 2), "decode_gbs": round(nbytes / t / 1e9, 1),
+          "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "decode_bytes": nbytes,
+          "dense_cache_us": round(t0 * 1e6, 2), "speedup_vs_dense": round(t0 / t, 3),
+          "ideal_speedup_bytes": round(nbytes0 / nbytes, 3), "compress_us": round(comp * 1e6, 1)})
+    del K, V, q, cache, cache0
+
+    # ---- sparsity sweeps ----
+    base = None
+    for tag in ("0", "50", "62p5", "75"):
+        w = synth.workload(f"sweep_decode_64k_b16_s{tag}")
+        G = w.hq // w.hkv
+        K, V, Q, q, shp, cnt, cache, comp = setup(w)
+        del Q
+        t = decode_time(shp, cnt, cache, q)
+        base = base or (t, decode_bytes(w, G))
+        nbytes = decode_bytes(w, G)
+        emit({"suite": w.name, "decode_us": round(t * 1e6, 2),
+              "decode_gbs": round(nbytes / t / 1e9, 1),
+              "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+              "speedup_vs_0pct": round(base[0] / t, 3),
+              "ideal_speedup_bytes": round(base[1] / nbytes, 3),
+              "compress_us": round(comp * 1e6, 1),
+              "compress_gbs": round(compress_bytes(w, hs.hs_cache_sizes(shp, cnt)) / comp / 1e9, 1)})
+        del K, V, q, cache
+    base = None
+    for tag in ("0", "50", "62p5", "75"):
+        w = synth.workload(f"sweep_prefill_32k_b1_s{tag}")
+        K, V, Q, q, shp, cnt, cache, comp = setup(w)
+        mk, mv = cache["map_k"].cpu().numpy(), cache["map_v"].cpu().numpy()
+        t = prefill_time(shp, cnt, cache, Q, hs.HS_PREFILL_SMFMAC)
+        dense_eq, ex, full = prefill_flops(w, mk, mv, True)
+        base = base or (t, ex)
+        emit({"suite": w.name, "prefill_ms": round(t * 1e3, 3),
+              "tflops_dense_equivalent": round(dense_eq / t / 1e12, 1),
+              "mfma_utilisation": round(ex / (BF16_DENSE_PEAK_TFLOPS * 1e12) / t, 4),
+              "speedup_vs_0pct": round(base[0] / t, 3),
+              "ideal_speedup_executed_flops": round(base[1] / ex, 3),
+              "compress_us": round(comp * 1e6, 1), "compress_share_of_prefill": round(comp / t, 5)})
+        del K, V, Q, q, cache
+    return 0
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
+    if args.suite:
+        return run_suite()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -276,7 +406,7 @@ def main():
     # written back to HBM during whatever kernel runs next. A read pass over a buffer larger than
     # that cache, between prefill and decode (inside the step, outside both kernels' windows),
     # settles them, so the decode window measures the decode's own reads.
-    settle = torch.ones(SETTLE_BYTES // 4, device=dev, dtype=torch.int32)
+    settle = torch.ones(SETTLE_BYTES // 4, device=dev, dtype=torch.float32)
 
     def step(ev=None):
         if ev:
