@@ -36,6 +36,7 @@ constexpr int kVReg = 16 * 1024;             // V region of a stage
 constexpr int kVMeta = 8 * 1024;             // 2:4 V metadata inside the V region
 constexpr int kStage = 32 * 1024;            // one tile: K 16 KB + V 16 KB (dense)
 constexpr int kListCap = 1024;               // visible blocks listed per pass
+constexpr int kScanChunks = 8;               // 64-block map chunks loaded per scan round
 constexpr int kListOff = 2 * kStage;         // map entries of the listed blocks (K, then V)
 constexpr int kLdsDec = kListOff + 2 * kListCap * 4;
 
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   // w_j the load count of visible block j, p_j the sum of w over the blocks before it and W the sum
   // over the head, block j belongs to split floor((2 p_j + w_j) S / 2W) -- the split whose share of
   // W holds the block's midpoint (clamped to the last split). The blocks are listed in LDS a batch
-  // of four 64-block chunks at a time, in passes of at most kListCap entries.
+  // of kScanChunks 64-block chunks at a time, in passes of at most kListCap entries.
   const int32_t *mkh = a.c.map_k + (size_t)head * a.nb;
   const int32_t *mvh = a.c.map_v + (size_t)head * a.nb;
   const int64_t two_w = 2 * (int64_t)a.total_w;
@@ -268,16 +269,16 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   bool finished = a.total_w <= 0;
   while (!finished) {
     int got = 0;  // blocks listed in this pass
-    while (!finished && got <= kListCap - 256) {
-      int mkv[4], mvv[4];
+    while (!finished && got <= kListCap - 64 * kScanChunks) {
+      int mkv[kScanChunks], mvv[kScanChunks];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kScanChunks; ++i) {
         const int j = scan + 64 * i + lane;
         mkv[i] = j < a.nb ? mkh[j] : 0;
         mvv[i] = j < a.nb ? mvh[j] : 0;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kScanChunks; ++i) {
         if (finished) break;
         const int w = mkv[i] != 0 ? TPB * tile_loads<B>(mkv[i], mvv[i]) : 0;
         int incl = w;
