@@ -32,6 +32,29 @@ __device__ __forceinline__ void score_group(uint32_t x0, uint32_t x1, uint32_t x
           ((keep & 8u) ? 0ull : f3);
 }
 
+// Fast form of the same keys for magnitudes below 256 (bf16 magnitude bits a < 0x4380): the bf16
+// bits are the high half of the fp32 value, and adding 24 to the fp32 exponent field scales it by
+// 2^24 exactly, so the truncating conversion gives floor(|x| * 2^24) < 2^32. Zero and denormal
+// inputs become tiny normal values that truncate to 0, their floor as well. At or above 256 the
+// conversion saturates to 0xFFFFFFFF, above every in-range key (255 * 2^24 = 0xFF000000): the
+// caller detects that and redoes the block with score_group.
+__device__ __forceinline__ uint32_t fixed_mag_small(uint32_t a) {
+  return (uint32_t)__uint_as_float((a << 16) + (24u << 23));
+}
+// The two dropped values of a group are its two smallest keys (the key is monotone in the
+// magnitude, and which of two equal magnitudes is dropped does not change the sum).
+__device__ __forceinline__ void score_group_fast(uint32_t x0, uint32_t x1, uint32_t x2,
+                                                 uint32_t x3, uint64_t &drop, uint64_t &all,
+                                                 uint32_t &fmax) {
+  const uint32_t f0 = fixed_mag_small(x0 & 0x7FFFu), f1 = fixed_mag_small(x1 & 0x7FFFu);
+  const uint32_t f2 = fixed_mag_small(x2 & 0x7FFFu), f3 = fixed_mag_small(x3 & 0x7FFFu);
+  const uint32_t l1 = min(f0, f1), h1 = max(f0, f1), l2 = min(f2, f3), h2 = max(f2, f3);
+  all += ((uint64_t)f0 + f1) + ((uint64_t)f2 + f3);
+  drop += (uint64_t)min(l1, l2) + min(max(l1, l2), min(h1, h2));
+  fmax = max(fmax, max(h1, h2));
+}
+constexpr uint32_t kMaxSmallKey = 0xFF000000u;  // floor(255 * 2^24), the largest fast-path key
+
 __device__ __forceinline__ uint32_t elem(const uint4 &v, int e) {
   uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
@@ -45,6 +68,7 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
   const size_t base = (size_t)blockIdx.y * L * kD + (size_t)i * B * kD;
   const uint16_t *Kb = K + base, *Vb = V + base;
   uint64_t kk = 0, kv = 0, kp = 0;
+  uint32_t fmax = 0;
   const int c8 = tid & 15;  // eight consecutive channels
 #pragma unroll
   for (int g = tid >> 4; g < B / 4; g += 16) {  // four consecutive tokens
@@ -56,12 +80,35 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // K: groups of four channels of one token
-      score_group(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk, kp);
-      score_group(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk, kp);
+      score_group_fast(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk,
+                       kp, fmax);
+      score_group_fast(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk,
+                       kp, fmax);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)  // V: groups of four tokens of one channel
-      score_group(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp);
+      score_group_fast(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp,
+                       fmax);
+  }
+  if (__ballot(fmax > kMaxSmallKey) != 0) {
+    // A magnitude of 256 or more in this wave's share: redo the share with the 64-bit keys.
+    kk = kv = kp = 0;
+    for (int g = tid >> 4; g < B / 4; g += 16) {
+      uint4 kr[4], vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kr[r] = *reinterpret_cast<const uint4 *>(Kb + (size_t)(4 * g + r) * kD + 8 * c8);
+        vr[r] = *reinterpret_cast<const uint4 *>(Vb + (size_t)(4 * g + r) * kD + 8 * c8);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        score_group(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk, kp);
+        score_group(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk, kp);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        score_group(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp);
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {

@@ -78,3 +78,31 @@ def test_compress_deterministic():
     a = gu.cache_to_numpy(gu.gpu_compress(shp, cnt, Kd, Vd))
     b = gu.cache_to_numpy(gu.gpu_compress(shp, cnt, Kd, Vd))
     gu.compare_cache(a, b)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_compress_keys_bit_exact(B):
+    """The per-block loss keys themselves (not only the ranking they lead to) equal the oracle's:
+    N(0,1) data with a few magnitudes of 256 and more in some blocks, so that within one launch
+    some waves take the 32-bit key path and others its 64-bit fallback."""
+    rng = np.random.default_rng(31 + B)
+    b, hkv, L = 2, 2, B * 9
+    Kf = rng.standard_normal((b, hkv, L, 128), dtype=np.float32)
+    Vf = rng.standard_normal((b, hkv, L, 128), dtype=np.float32)
+    Kf[0, 0, 3, 5] = 300.0
+    Kf[1, 1, 4 * B + 7, 100] = -4096.0
+    Vf[0, 1, 2 * B + 1, 64] = 257.0
+    Vf[1, 0, 5 * B, 0] = 1.0e6
+    Kf[0, 1, 6 * B + 2, 9] = 255.0  # the largest magnitude of the fast path
+    K, V = synth.bf16_bits(Kf), synth.bf16_bits(Vf)
+    counts = (1, 3, 4)
+    shp, cnt = hs.shape(b, hkv, hkv, L, 128, B), hs.counts(*counts)
+    cache = hs.alloc_cache(shp, cnt)
+    ws = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+    hs.hs_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V), cache, ws)
+    torch.cuda.synchronize()
+    nb = L // B
+    got = ws[: b * hkv * nb * 3 * 8].cpu().numpy().view(np.uint64).reshape(b, hkv, nb, 3)
+    want = oracle.compress(Dims(b, hkv, L, 128, B, *counts), K, V)
+    assert np.array_equal(got, want["keys"]), np.argwhere(got != want["keys"])[:8]
+    gu.compare_cache(gu.cache_to_numpy(cache), want)
