@@ -14,10 +14,11 @@
 //
 // Per visible 64-token KV tile n (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 and
 // v_smfmac_f32_32x32x32_bf16; all accumulators in VGPRs):
-//   staging   four LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) two
-//             tiles ahead; one barrier per tile. A stage holds the tile's K and V^T in their stored
-//             representation (dense copy, or kept values + metadata), rows padded by 16 bytes so
-//             that the operand reads are free of bank conflicts with plain immediate offsets.
+//   staging   three LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) one
+//             tile ahead; one wait for the wave's loads and one barrier per tile. A stage holds
+//             the tile's K and V^T in their stored representation (dense copy, or kept values +
+//             metadata), rows padded by 16 bytes so that the operand reads are free of bank
+//             conflicts with plain immediate offsets.
 //   GEMM1     S^T[64 tok][32 q] = K Q^T (Q stays in registers as the B operand).
 //   softmax   causal mask, column-wise running max (exp2 domain, lazy rescale) and
 //             P^T = exp2(S^T - max) packed to bf16 in registers.
@@ -39,7 +40,7 @@ constexpr int kD = 128;
 constexpr int kTile = 64;   // KV tokens per tile
 constexpr int kQTile = 32;  // queries per wave
 constexpr int kWaves = 8;
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 
 // ---- LDS stage layout (bytes). Rows are padded by one 16-byte unit: with a stride of 17, 9 or 5
 // units, 16 consecutive rows read at one column hit 16 distinct bank groups.
@@ -56,8 +57,13 @@ constexpr int kVMetaOff = kVnUnits * 16;          // 2:4 V metadata: 128 ch x 8 
 constexpr int kKRegion = kKdUnits * 16;           // 17408
 constexpr int kVRegion = kVdUnits * 16;           // 18432
 constexpr int kStageBytes = kKRegion + kVRegion;  // 35840
-constexpr int kMapOff = kStages * kStageBytes;    // per-block local slots, int16
-constexpr int kLdsBytes = kMapOff + 2 * kMaxBlocks * 2;  // 156 KB
+// The workgroup's visible blocks in order: their modes as local pool slots (int32: K slot code in
+// the high half, V slot code in the low half; +(i+1) dense slot i, -(i+1) 2:4 slot i) and their
+// block indices (int16), plus the per-wave counts used while building the list.
+constexpr int kListModesOff = kStages * kStageBytes;
+constexpr int kListBlkOff = kListModesOff + 4 * kMaxBlocks;
+constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
+constexpr int kLdsBytes = kCountOff + 4 * kWaves;  // 129 KB
 static_assert(kKdUnits % 64 == 0 && kVdUnits % 64 == 0 && kKnUnits % 64 == 0 &&
                   kVnUnits % 64 == 0, "whole 1 KB loads");
 static_assert(kKMetaOff + 1024 <= kKRegion && kVMetaOff + 1024 <= kVRegion, "metadata fits");
@@ -330,15 +336,6 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev
 // region goes to wave q % 8. Pad units receive a copy of a real unit of the same row. Metadata:
 // K (1 KB) by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves
 // 3-6 (block 128, where a tile is half of each channel's metadata row).
-template <int B>
-__device__ __forceinline__ int dma_count(int wave, bool dense_k, bool dense_v) {
-  const int k = dense_k ? (kKdUnits / 64 + 7 - wave) / 8
-                        : (kKnUnits / 64 + 7 - wave) / 8 + (wave == 1 ? 1 : 0);
-  const int v = dense_v ? (kVdUnits / 64 + 7 - wave) / 8
-                        : (kVnUnits / 64 + 7 - wave) / 8 +
-                              (B == 64 ? (wave == 2 ? 1 : 0) : (wave >= 3 && wave <= 6 ? 1 : 0));
-  return k + v;
-}
 
 template <int B, bool kSmfmac>
 __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
@@ -364,17 +361,39 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   const int kt_max = (kQTile * qt_max + kQTile - 1) / kTile;
   const int nbq = kt_max / TPB + 1;  // blocks touched by this workgroup
 
-  // Block modes of this head as local pool slots: +(i+1) dense slot i, -(i+1) 2:4 slot i, 0 pruned.
-  int16_t *mk16 = reinterpret_cast<int16_t *>(lds + kMapOff);
-  int16_t *mv16 = mk16 + kMaxBlocks;
+  // The visible blocks of this head up to the workgroup's last key tile, compacted in order
+  // (ballot per wave, then the counts of the lower waves as the offset).
+  int32_t *lmodes = reinterpret_cast<int32_t *>(lds + kListModesOff);
+  int16_t *lblk = reinterpret_cast<int16_t *>(lds + kListBlkOff);
+  int32_t *wcount = reinterpret_cast<int32_t *>(lds + kCountOff);
+  int n_vis = 0;
   {
     const int32_t *mkh = a.c.map_k + (size_t)head * a.nb, *mvh = a.c.map_v + (size_t)head * a.nb;
-    for (int i = tid; i < nbq; i += kWaves * 64) {
-      const int mk = mkh[i], mv = mvh[i];
-      mk16[i] = (int16_t)(mk > 0 ? mk - head * a.ndk : (mk < 0 ? mk + head * a.nsk : 0));
-      mv16[i] = (int16_t)(mv > 0 ? mv - head * a.ndv : (mv < 0 ? mv + head * a.nsv : 0));
+    for (int base = 0; base < nbq; base += kWaves * 64) {
+      const int j = base + tid;
+      const int mk = j < nbq ? mkh[j] : 0, mv = j < nbq ? mvh[j] : 0;
+      const uint64_t vis = __builtin_amdgcn_ballot_w64(mk != 0);
+      const int rank = __builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(vis >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vis, 0u));
+      if (lane == 0) wcount[wave] = __builtin_popcountll(vis);
+      __syncthreads();
+      int off = n_vis;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const int cw = wcount[w2];
+        off += w2 < wave ? cw : 0;
+        n_vis += cw;
+      }
+      if (mk != 0) {
+        const int sk = mk > 0 ? mk - head * a.ndk : mk + head * a.nsk;
+        const int sv = mv > 0 ? mv - head * a.ndv : mv + head * a.nsv;
+        lmodes[off + rank] = (sk << 16) | (sv & 0xFFFF);
+        lblk[off + rank] = (int16_t)j;
+      }
+      __syncthreads();  // list entries visible; counts free for the next round
     }
   }
+  n_vis = __builtin_amdgcn_readfirstlane(n_vis);
 
   WaveState w;
   {
@@ -404,14 +423,19 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
 
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
 
-  __syncthreads();  // block modes visible
-
-  auto mode_k = [&](int kt) { return __builtin_amdgcn_readfirstlane(mk16[kt / TPB]); };
-  auto mode_v = [&](int kt) { return __builtin_amdgcn_readfirstlane(mv16[kt / TPB]); };
-  auto next_visible = [&](int kt) {
-    while (kt <= kt_max && mode_k(kt) == 0) ++kt;
-    return kt;
+  // Tile t of the walk: half t % TPB of visible block t / TPB (block modes mk, mv as slot codes).
+  auto tile_info = [&](int t, int &kt, int &mk, int &mv) {
+    const int i = t / TPB;
+    const int e = __builtin_amdgcn_readfirstlane(lmodes[i]);
+    kt = __builtin_amdgcn_readfirstlane((int)lblk[i]) * TPB + t % TPB;
+    mk = e >> 16;
+    mv = (int)(int16_t)(e & 0xFFFF);
   };
+  // The last visible block can reach past the last key tile (block 128: its second half).
+  const int n_tiles =
+      n_vis == 0 ? 0
+                 : n_vis * TPB - ((__builtin_amdgcn_readfirstlane((int)lblk[n_vis - 1]) + 1) *
+                                          TPB - 1 > kt_max ? 1 : 0);
   // Per-lane global byte offsets of this wave's direct loads (load q = wave + 8 i of a region),
   // computed once: [i] for the padded dense/2:4 rows, for both GEMM1 row orders of K (see tau).
   uint32_t oKd[2][3], oKn[2][2], oKm[2], oVd[3], oVn[2], oVm;
@@ -421,67 +445,75 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
       auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, sp); };
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
-        const int u = 64 * (wave + kWaves * i) + lane, row = u / 17, cu = u - 17 * row;
+        const int u = 64 * min(wave + kWaves * i, kKdUnits / 64 - 1) + lane, row = u / 17,
+                  cu = u - 17 * row;
         oKd[sp][i] = token(min(row, 63)) * 256 + 16 * min(cu, 15);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int u = 64 * (wave + kWaves * i) + lane, row = u / 9, cu = u - 9 * row;
+        const int u = 64 * min(wave + kWaves * i, kKnUnits / 64 - 1) + lane, row = u / 9,
+                  cu = u - 9 * row;
         oKn[sp][i] = token(min(row, 63)) * 128 + 16 * min(cu, 7);
       }
       oKm[sp] = token(lane) * 16;
     }
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int u = 64 * (wave + kWaves * i) + lane, ch = u / 9, cu = u - 9 * ch;
+      const int u = 64 * min(wave + kWaves * i, kVdUnits / 64 - 1) + lane, ch = u / 9,
+                cu = u - 9 * ch;
       oVd[i] = min(ch, 127) * (2 * B) + 16 * min(cu, 7);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int u = 64 * (wave + kWaves * i) + lane, ch = u / 5, cu = u - 5 * ch;
+      const int u = 64 * min(wave + kWaves * i, kVnUnits / 64 - 1) + lane, ch = u / 5,
+                cu = u - 5 * ch;
       oVn[i] = min(ch, 127) * B + 16 * min(cu, 3);
     }
     const int d = 64 * ((wave + 5) & 3) + lane;  // block 128: waves 3..6 -> dword loads 0..3
     oVm = B == 64 ? 16 * lane : (d >> 1) * (B / 8) + 4 * (d & 1);
   }
 
-  // Direct loads of one tile (block modes mk, mv) into a stage.
+  // Direct loads of one tile (block modes mk, mv) into a stage. Every wave issues the same number
+  // of loads per region; a wave with no load left repeats the region's last one (same source,
+  // same destination, same bytes), so the issue has no per-load branches.
+  const uint16_t *kd_h = a.c.k_dense + (size_t)head * a.ndk * B * kD;
+  const uint16_t *kn_h = a.c.k_nnz + (size_t)head * a.nsk * B * (kD / 2);
+  const uint16_t *km_h = a.c.k_meta + (size_t)head * a.nsk * B * (kD / 16);
+  const uint16_t *vd_h = a.c.v_dense + (size_t)head * a.ndv * B * kD;
+  const uint16_t *vn_h = a.c.v_nnz + (size_t)head * a.nsv * B * (kD / 2);
+  const uint16_t *vm_h = a.c.v_meta + (size_t)head * a.nsv * B * (kD / 16);
   auto issue = [&](int kt, int mk, int mv, int stage) {
     const int half = kt % TPB;
     const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kKRegion;
     const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
     if (mk > 0) {
-      const char *g = uniform_ptr(
-          a.c.k_dense + ((size_t)(head * a.ndk + mk - 1) * B + kTile * half) * kD);
+      const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
 #pragma unroll
       for (int i = 0; i < 3; ++i)
-        if (wave + kWaves * i < kKdUnits / 64)
-          dma16(g, sp ? oKd[1][i] : oKd[0][i], kl + 1024 * (wave + kWaves * i));
+        dma16(g, sp ? oKd[1][i] : oKd[0][i],
+              kl + 1024 * min(wave + kWaves * i, kKdUnits / 64 - 1));
     } else {
-      const size_t row0 = (size_t)(head * a.nsk - mk - 1) * B + kTile * half;
-      const char *g = uniform_ptr(a.c.k_nnz + row0 * (kD / 2));
+      const int row0 = (-mk - 1) * B + kTile * half;
+      const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (wave + kWaves * i < kKnUnits / 64)
-          dma16(g, sp ? oKn[1][i] : oKn[0][i], kl + 1024 * (wave + kWaves * i));
+        dma16(g, sp ? oKn[1][i] : oKn[0][i],
+              kl + 1024 * min(wave + kWaves * i, kKnUnits / 64 - 1));
       if (wave == 1)
-        dma16(uniform_ptr(a.c.k_meta + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kKMetaOff);
+        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kKMetaOff);
     }
     if (mv > 0) {
-      const char *g = uniform_ptr(a.c.v_dense + (size_t)(head * a.ndv + mv - 1) * B * kD +
-                                  kTile * half);
+      const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
 #pragma unroll
       for (int i = 0; i < 3; ++i)
-        if (wave + kWaves * i < kVdUnits / 64)
-          dma16(g, oVd[i], vl + 1024 * (wave + kWaves * i));
+        dma16(g, oVd[i], vl + 1024 * min(wave + kWaves * i, kVdUnits / 64 - 1));
     } else {
-      const size_t blk0 = (size_t)(head * a.nsv - mv - 1) * B * kD;
-      const char *g = uniform_ptr(a.c.v_nnz + blk0 / 2 + (kTile / 2) * half);
+      const int blk = (-mv - 1) * B * kD;
+      const char *g = uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (wave + kWaves * i < kVnUnits / 64)
-          dma16(g, oVn[i], vl + 1024 * (wave + kWaves * i));
-      const char *gm = uniform_ptr(a.c.v_meta + blk0 / 16 + (kTile / 16) * half);
+        dma16(g, oVn[i], vl + 1024 * min(wave + kWaves * i, kVnUnits / 64 - 1));
+      const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
       if (B == 64) {
         if (wave == 2) dma16(gm, oVm, vl + kVMetaOff);
       } else if (wave >= 3 && wave <= 6) {
@@ -490,27 +522,28 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     }
   };
   const float c = a.scale_log2;
-  // Tiles n, n+1, n+2 of the walk with their block modes (kt > kt_max: none).
-  int kt0 = next_visible(0);
-  int kt1 = kt0 <= kt_max ? next_visible(kt0 + 1) : kt_max + 1;
-  int mk0 = kt0 <= kt_max ? mode_k(kt0) : 0, mv0 = kt0 <= kt_max ? mode_v(kt0) : 0;
-  int mk1 = kt1 <= kt_max ? mode_k(kt1) : 0, mv1 = kt1 <= kt_max ? mode_v(kt1) : 0;
-  if (kt0 <= kt_max) issue(kt0, mk0, mv0, 0);
-  if (kt1 <= kt_max) issue(kt1, mk1, mv1, 1);
+  // Tile it of the walk is computed from stage it % 3 while tile it + 1 lands in the next stage.
+  int kt0 = 0, mk0 = 0, mv0 = 0;
+  if (n_tiles > 0) {
+    tile_info(0, kt0, mk0, mv0);
+    issue(kt0, mk0, mv0, 0);
+  }
 
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
   bool prev_sparse_v = false;
   const char *st_prev = lds;
-  int it = 0;
-  while (kt0 <= kt_max) {
-    const int kt2 = kt1 <= kt_max ? next_visible(kt1 + 1) : kt_max + 1;
-    const int mk2 = kt2 <= kt_max ? mode_k(kt2) : 0, mv2 = kt2 <= kt_max ? mode_v(kt2) : 0;
-    wait_vmem(kt1 <= kt_max ? dma_count<B>(wave, mk1 > 0, mv1 > 0) : 0);
-    barrier();  // tile kt0 staged by every wave; stage (it + 2) % 4 no longer read
-    if (kt2 <= kt_max) issue(kt2, mk2, mv2, (it + 2) & 3);
+  int stage = 0;
+  for (int it = 0; it < n_tiles; ++it) {
+    int kt1 = 0, mk1 = 0, mv1 = 0;
+    const bool more = it + 1 < n_tiles;
+    if (more) tile_info(it + 1, kt1, mk1, mv1);
+    const int next_stage = stage == kStages - 1 ? 0 : stage + 1;
+    wait_vmem(0);  // this wave's loads of tile it have landed
+    barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
+    if (more) issue(kt1, mk1, mv1, next_stage);
 
-    const char *st = lds + (it & 3) * kStageBytes;
+    const char *st = lds + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
       gemm1<true, kSmfmac>(w, st, lo, hf);
@@ -522,16 +555,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
     st_prev = st;
+    stage = next_stage;
     kt0 = kt1;
     mk0 = mk1;
     mv0 = mv1;
-    kt1 = kt2;
-    mk1 = mk2;
-    mv1 = mv2;
-    ++it;
   }
   // GEMM2 of the last tile (its stage is not overwritten after the loop).
-  if (it > 0) {
+  if (n_tiles > 0) {
     uint2 meta[4];
     load_vmeta(meta, st_prev, prev_sparse_v, lo);
 #pragma unroll
