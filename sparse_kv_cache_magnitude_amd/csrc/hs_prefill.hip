@@ -42,31 +42,29 @@ constexpr int kQTile = 32;  // queries per wave
 constexpr int kWaves = 8;
 constexpr int kStages = 3;
 
-// ---- LDS stage layout (bytes). Rows are padded by one 16-byte unit: with a stride of 17, 9 or 5
-// units, 16 consecutive rows read at one column hit 16 distinct bank groups.
-constexpr int kKdStride = 272;                    // dense K row: 64 tok x (256 + 16)
-constexpr int kKnStride = 144;                    // 2:4 K values row: 64 tok x (128 + 16)
-constexpr int kVdStride = 144;                    // dense V^T row: 128 ch x (128 + 16)
-constexpr int kVnStride = 80;                     // 2:4 V^T values row: 128 ch x (64 + 16)
-constexpr int kKdUnits = 64 * kKdStride / 16;     // 1088 sixteen-byte units (17 loads)
-constexpr int kKnUnits = 64 * kKnStride / 16;     // 576 (9 loads)
-constexpr int kVdUnits = 128 * kVdStride / 16;    // 1152 (18 loads)
-constexpr int kVnUnits = 128 * kVnStride / 16;    // 640 (10 loads)
-constexpr int kKMetaOff = kKnUnits * 16;          // 2:4 K metadata: 64 tok x 16 B
-constexpr int kVMetaOff = kVnUnits * 16;          // 2:4 V metadata: 128 ch x 8 B
-constexpr int kKRegion = kKdUnits * 16;           // 17408
-constexpr int kVRegion = kVdUnits * 16;           // 18432
-constexpr int kStageBytes = kKRegion + kVRegion;  // 35840
+// ---- LDS stage layout (bytes). A stage holds one tile in two 16 KB regions:
+//   K region   dense: 64 rows x 256 B; 2:4: 64 rows x 128 B of kept values and the 2:4 K
+//              metadata (64 x 16 B) at kMetaOff
+//   V^T region dense: 128 rows x 128 B; 2:4: 128 rows x 64 B of kept values in 32-row groups
+//              4 KB apart (as for dense, so both kinds address a 32-channel tile alike), and the
+//              2:4 V metadata (128 x 8 B) in the free half of the first group, at kVMetaOff
+// Rows are not padded: the 16-byte units of row r are stored at unit u ^ f(r), with f chosen so
+// that 16 consecutive rows read at one logical unit hit 16 distinct bank groups (f = r & 15 for
+// 16-unit rows, (r >> 1) & 7 for 8-unit rows, (r >> 2) & 3 for 4-unit rows). Every region is a
+// whole number of 1 KB direct loads per wave: dense 2, 2:4 values 1.
+constexpr int kRegion = 16384;
+constexpr int kStageBytes = 2 * kRegion;  // 32 KB
+constexpr int kMetaOff = 8192;            // K region: 2:4 K metadata
+constexpr int kCtStride = 4096;           // V^T region: bytes between 32-channel tiles
+constexpr int kVMetaOff = kRegion + 2048;  // stage: 2:4 V metadata
 // The workgroup's visible blocks in order: their modes as local pool slots (int32: K slot code in
 // the high half, V slot code in the low half; +(i+1) dense slot i, -(i+1) 2:4 slot i) and their
 // block indices (int16), plus the per-wave counts used while building the list.
 constexpr int kListModesOff = kStages * kStageBytes;
 constexpr int kListBlkOff = kListModesOff + 4 * kMaxBlocks;
 constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
-constexpr int kLdsBytes = kCountOff + 4 * kWaves;  // 129 KB
-static_assert(kKdUnits % 64 == 0 && kVdUnits % 64 == 0 && kKnUnits % 64 == 0 &&
-                  kVnUnits % 64 == 0, "whole 1 KB loads");
-static_assert(kKMetaOff + 1024 <= kKRegion && kVMetaOff + 1024 <= kVRegion, "metadata fits");
+constexpr int kLdsBytes = kCountOff + 4 * kWaves;  // 120 KB
+static_assert(kRegion / 1024 == 2 * kWaves && kMetaOff / 1024 == kWaves, "loads per wave");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
@@ -100,8 +98,17 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-__device__ __forceinline__ uint4 lds16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ uint2 lds8(const char *p) { return *reinterpret_cast<const uint2 *>(p); }
+// LDS reads by byte address (the stage base plus a lane offset).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 lds16(uint32_t a) {
+  const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(size_t)a;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 lds8(uint32_t a) {
+  const u32x2 v = *(__attribute__((address_space(3))) const u32x2 *)(size_t)a;
+  return make_uint2(v.x, v.y);
+}
 
 // Two packed 2:4 groups (4 kept values as two dwords, 8 metadata bits) -> 8 dense values.
 __device__ __forceinline__ bf16x8 expand2(uint2 v, uint32_t bits) {
@@ -141,46 +148,48 @@ struct WaveState {
   float m_run, l_run, m_use, alpha;
 };
 
-// Per-lane LDS byte offsets of the operand reads, relative to a stage.
+// Per-lane LDS byte offsets of the operand reads, relative to a stage, with the lane's part of
+// the unit swizzle folded in; a read XORs in the (compile-time) unit of its k-step and adds the
+// row-group offset.
 struct LaneOffsets {
-  int kd, kn, km;  // dense K rows, 2:4 K values, 2:4 K metadata
-  int vd, vn, vm;  // dense V^T rows, 2:4 V^T values, 2:4 V^T metadata
+  int kd, kn, knd, km;  // dense K; 2:4 K values for SMFMAC (16 B) and decompress (8 B); metadata
+  int vd, vdd, vn, vnd, vm;  // dense V^T split (SMFMAC) and dense (decompress); 2:4 V^T; metadata
 };
 
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
 // Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
 template <bool kSparseK, bool kSmfmac>
-__device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOffsets &lo,
-                                      int hf) {
+__device__ __forceinline__ void gemm1(WaveState &w, uint32_t sb, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     f32x16 acc = zero16();
     if (!kSparseK) {
-      const char *rp = st + lo.kd + T * 32 * kKdStride;
+      const uint32_t b = sb + lo.kd;
       uint4 k[8];  // all reads issued before the first MFMA that needs them
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16(rp + 32 * ks);
+      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16((b ^ (32 * ks)) + T * 8192);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         acc = mfma32(as_bf16x8(k[ks]), half8(w.qv[ks >> 1], ks & 1), acc);
     } else {
-      const char *rp = st + lo.kn + T * 32 * kKnStride;
-      const uint4 meta = lds16(st + lo.km + T * 32 * 16);
+      const uint4 meta = lds16(sb + lo.km + T * 512);
       const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
       if (kSmfmac) {
+        const uint32_t b = sb + lo.kn;
         uint4 k[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) k[u] = lds16(rp + 32 * u);
+        for (int u = 0; u < 4; ++u) k[u] = lds16((b ^ (32 * u)) + T * 4096);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           acc = smfmac32(as_bf16x8(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
       } else {
-        // Decompress: the lane's 8-byte half of 16-byte unit ks (lo.kn carries +16 per half).
-        const char *rq = rp - 8 * hf;
+        // Decompress: the lane's 8-byte half of 16-byte unit ks.
+        const uint32_t b = sb + lo.knd;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const uint32_t bits = (mw[ks >> 1] >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          acc = mfma32(expand2(lds8(rq + 16 * ks), bits), half8(w.qv[ks >> 1], ks & 1), acc);
+          acc = mfma32(expand2(lds8((b ^ (16 * ks)) + T * 4096), bits),
+                       half8(w.qv[ks >> 1], ks & 1), acc);
         }
       }
     }
@@ -194,39 +203,38 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOf
 // lane's tokens 0..7 at group positions {0,1}, index 0x4444), and for a dense tile a second one on
 // tokens 8..15 at positions {2,3} (index 0xEEEE). For a dense tile P^T arrives in the matching
 // token order (tau with bits 1 and 3 exchanged).
-__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, const char *st, bool sparse,
+__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, uint32_t sb, bool sparse,
                                                   const uint2 *meta, int u, const LaneOffsets &lo,
                                                   int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const char *a = sparse ? st + lo.vn + ct * 32 * kVnStride + 32 * u
-                           : st + lo.vd + ct * 32 * kVdStride + 64 * u;
+    const uint32_t a = (sparse ? ((sb + lo.vn) ^ (32 * u)) : ((sb + lo.vd) ^ (64 * u))) +
+                       ct * kCtStride;
     const uint32_t idx = sparse ? ((u ? meta[ct].y : meta[ct].x) >> (16 * hf)) : 0x4444u;
     w.o[ct] = smfmac32(as_bf16x8(lds16(a)), w.p[u], idx, w.o[ct]);
-    if (!sparse) w.o[ct] = smfmac32(as_bf16x8(lds16(a + 16)), w.p[u], 0xEEEEu, w.o[ct]);
+    if (!sparse) w.o[ct] = smfmac32(as_bf16x8(lds16(a ^ 16)), w.p[u], 0xEEEEu, w.o[ct]);
   }
 }
-__device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
+__device__ __forceinline__ void load_vmeta(uint2 *meta, uint32_t sb, bool sparse,
                                            const LaneOffsets &lo) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
-    meta[ct] = sparse ? lds8(st + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
+    meta[ct] = sparse ? lds8(sb + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
 }
 
 // ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
 template <bool kSparseV>
-__device__ __forceinline__ void gemm2_dense_step(WaveState &w, const char *st, const uint2 *meta,
+__device__ __forceinline__ void gemm2_dense_step(WaveState &w, uint32_t sb, const uint2 *meta,
                                                  int ks, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     bf16x8 v;
     if (!kSparseV) {
-      // lo.vd carries +32 for lane half 1 (the split layout); a dense k-step wants +16.
-      v = as_bf16x8(lds16(st + lo.vd - 16 * hf + ct * 32 * kVdStride + 32 * ks));
+      v = as_bf16x8(lds16(((sb + lo.vdd) ^ (32 * ks)) + ct * kCtStride));
     } else {
       const uint32_t bits =
           (((ks >> 1) ? meta[ct].y : meta[ct].x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-      v = expand2(lds8(st + lo.vn - 8 * hf + ct * 32 * kVnStride + 16 * ks), bits);
+      v = expand2(lds8(((sb + lo.vnd) ^ (16 * ks)) + ct * kCtStride), bits);
     }
     w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
   }
@@ -298,16 +306,16 @@ __device__ __forceinline__ void softmax_finish(WaveState &w, bool need, float ls
 }
 
 template <bool kSmfmac>
-__device__ __forceinline__ void gemm2_u(WaveState &w, const char *st, bool sparse,
+__device__ __forceinline__ void gemm2_u(WaveState &w, uint32_t sb, bool sparse,
                                         const uint2 *meta, int u, const LaneOffsets &lo, int hf) {
   if (kSmfmac) {
-    gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
+    gemm2_smfmac_step(w, sb, sparse, meta, u, lo, hf);
   } else if (sparse) {
-    gemm2_dense_step<true>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<true>(w, st, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<true>(w, sb, meta, 2 * u, lo, hf);
+    gemm2_dense_step<true>(w, sb, meta, 2 * u + 1, lo, hf);
   } else {
-    gemm2_dense_step<false>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<false>(w, st, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<false>(w, sb, meta, 2 * u, lo, hf);
+    gemm2_dense_step<false>(w, sb, meta, 2 * u + 1, lo, hf);
   }
 }
 
@@ -315,16 +323,16 @@ __device__ __forceinline__ void gemm2_u(WaveState &w, const char *st, bool spars
 // instructions that read P^T of the previous tile are issued first, then the same registers
 // receive P^T of the current tile, 32 tokens at a time.
 template <bool kSmfmac>
-__device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev, bool gemm,
+__device__ __forceinline__ float exp_and_gemm2(WaveState &w, uint32_t sb_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
                                                float c) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
   uint2 meta[4];
-  load_vmeta(meta, st_prev, gemm && sparse, lo);
+  load_vmeta(meta, sb_prev, gemm && sparse, lo);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (gemm) gemm2_u<kSmfmac>(w, st_prev, sparse, meta, u, lo, hf);
+    if (gemm) gemm2_u<kSmfmac>(w, sb_prev, sparse, meta, u, lo, hf);
     softmax_exp(w, 2 * u, c, mc, lsum);
     softmax_exp(w, 2 * u + 1, c, mc, lsum);
   }
@@ -414,12 +422,18 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   w.l_run = 0.f;
 
   LaneOffsets lo;
-  lo.kd = r * kKdStride + 16 * hf;
-  lo.kn = r * kKnStride + 16 * hf;
-  lo.km = kKMetaOff + r * 16;
-  lo.vd = kKRegion + r * kVdStride + 32 * hf;
-  lo.vn = kKRegion + r * kVnStride + 16 * hf;
-  lo.vm = kKRegion + kVMetaOff + r * 8;
+  {
+    const int f16 = r & 15, f8 = (r >> 1) & 7, f4 = (r >> 2) & 3;
+    lo.kd = r * 256 + 32 * (f16 >> 1) + 16 * (hf ^ (f16 & 1));
+    lo.kn = r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
+    lo.knd = r * 128 + 16 * f8 + 8 * hf;
+    lo.km = kMetaOff + r * 16;
+    lo.vd = kRegion + r * 128 + 16 * ((2 * hf) ^ f8);
+    lo.vdd = kRegion + r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
+    lo.vn = kRegion + r * 64 + 32 * (f4 >> 1) + 16 * (hf ^ (f4 & 1));
+    lo.vnd = kRegion + r * 64 + 16 * f4 + 8 * hf;
+    lo.vm = kVMetaOff + r * 8;
+  }
 
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
 
@@ -436,46 +450,30 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
       n_vis == 0 ? 0
                  : n_vis * TPB - ((__builtin_amdgcn_readfirstlane((int)lblk[n_vis - 1]) + 1) *
                                           TPB - 1 > kt_max ? 1 : 0);
-  // Per-lane global byte offsets of this wave's direct loads (load q = wave + 8 i of a region),
-  // computed once: [i] for the padded dense/2:4 rows, for both GEMM1 row orders of K (see tau).
-  uint32_t oKd[2][3], oKn[2][2], oKm[2], oVd[3], oVn[2], oVm;
+  // Per-lane global byte offsets of this wave's direct loads: one per region (for K, one per
+  // GEMM1 row order, see tau). Load i of a dense region (LDS units 64 (wave + 8 i) + lane) is the
+  // same lane pattern 32 (K) or 64 (V^T) rows further on, a per-load constant.
+  uint32_t oKd[2], oKn[2], oKm[2], oVd, oVn, oVm;
   {
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
       auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, sp); };
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int u = 64 * min(wave + kWaves * i, kKdUnits / 64 - 1) + lane, row = u / 17,
-                  cu = u - 17 * row;
-        oKd[sp][i] = token(min(row, 63)) * 256 + 16 * min(cu, 15);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int u = 64 * min(wave + kWaves * i, kKnUnits / 64 - 1) + lane, row = u / 9,
-                  cu = u - 9 * row;
-        oKn[sp][i] = token(min(row, 63)) * 128 + 16 * min(cu, 7);
-      }
+      const int rd = 4 * wave + (lane >> 4), cd = lane & 15;   // dense K: 16 units per row
+      oKd[sp] = token(rd) * 256 + 16 * (cd ^ (rd & 15));
+      const int rn = 8 * wave + (lane >> 3), cn = lane & 7;    // 2:4 K: 8 units per row
+      oKn[sp] = token(rn) * 128 + 16 * (cn ^ ((rn >> 1) & 7));
       oKm[sp] = token(lane) * 16;
     }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int u = 64 * min(wave + kWaves * i, kVdUnits / 64 - 1) + lane, ch = u / 9,
-                cu = u - 9 * ch;
-      oVd[i] = min(ch, 127) * (2 * B) + 16 * min(cu, 7);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = 64 * min(wave + kWaves * i, kVnUnits / 64 - 1) + lane, ch = u / 5,
-                cu = u - 5 * ch;
-      oVn[i] = min(ch, 127) * B + 16 * min(cu, 3);
-    }
+    const int rd = 8 * wave + (lane >> 3), cd = lane & 7;      // dense V^T: 8 units per row
+    oVd = rd * (2 * B) + 16 * (cd ^ ((rd >> 1) & 7));
+    const int rn = 16 * wave + (lane >> 2), cn = lane & 3;     // 2:4 V^T: 4 units per row
+    oVn = rn * B + 16 * (cn ^ ((rn >> 2) & 3));
     const int d = 64 * ((wave + 5) & 3) + lane;  // block 128: waves 3..6 -> dword loads 0..3
     oVm = B == 64 ? 16 * lane : (d >> 1) * (B / 8) + 4 * (d & 1);
   }
 
-  // Direct loads of one tile (block modes mk, mv) into a stage. Every wave issues the same number
-  // of loads per region; a wave with no load left repeats the region's last one (same source,
-  // same destination, same bytes), so the issue has no per-load branches.
+  // Direct loads of one tile (block modes mk, mv) into a stage: dense regions two 1 KB loads per
+  // wave, 2:4 values one, metadata one load by one wave (block 128: four dword loads).
   const uint16_t *kd_h = a.c.k_dense + (size_t)head * a.ndk * B * kD;
   const uint16_t *kn_h = a.c.k_nnz + (size_t)head * a.nsk * B * (kD / 2);
   const uint16_t *km_h = a.c.k_meta + (size_t)head * a.nsk * B * (kD / 16);
@@ -484,40 +482,33 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   const uint16_t *vm_h = a.c.v_meta + (size_t)head * a.nsv * B * (kD / 16);
   auto issue = [&](int kt, int mk, int mv, int stage) {
     const int half = kt % TPB;
-    const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kKRegion;
+    const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kRegion;
     const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
     if (mk > 0) {
       const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        dma16(g, sp ? oKd[1][i] : oKd[0][i],
-              kl + 1024 * min(wave + kWaves * i, kKdUnits / 64 - 1));
+      const uint32_t o = sp ? oKd[1] : oKd[0];
+      dma16(g, o, kl + 1024 * wave);
+      dma16(g + 32 * 2 * kD, o, kl + 1024 * (wave + kWaves));
     } else {
       const int row0 = (-mk - 1) * B + kTile * half;
-      const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(g, sp ? oKn[1][i] : oKn[0][i],
-              kl + 1024 * min(wave + kWaves * i, kKnUnits / 64 - 1));
+      dma16(uniform_ptr(kn_h + row0 * (kD / 2)), sp ? oKn[1] : oKn[0], kl + 1024 * wave);
       if (wave == 1)
-        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kKMetaOff);
+        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        dma16(g, oVd[i], vl + 1024 * min(wave + kWaves * i, kVdUnits / 64 - 1));
+      dma16(g, oVd, vl + 1024 * wave);
+      dma16(g + 64 * 2 * B, oVd, vl + 1024 * (wave + kWaves));
     } else {
       const int blk = (-mv - 1) * B * kD;
-      const char *g = uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(g, oVn[i], vl + 1024 * min(wave + kWaves * i, kVnUnits / 64 - 1));
+      // 16 rows per load; rows 32 ct + .. start at ct * kCtStride.
+      dma16(uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half), oVn,
+            vl + (wave >> 1) * kCtStride + 1024 * (wave & 1));
       const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
       if (B == 64) {
-        if (wave == 2) dma16(gm, oVm, vl + kVMetaOff);
+        if (wave == 2) dma16(gm, oVm, kl + kVMetaOff);
       } else if (wave >= 3 && wave <= 6) {
-        dma4(gm, oVm, vl + kVMetaOff + 256 * (wave - 3));
+        dma4(gm, oVm, kl + kVMetaOff + 256 * (wave - 3));
       }
     }
   };
@@ -532,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
   bool prev_sparse_v = false;
-  const char *st_prev = lds;
+  uint32_t sb_prev = lds_base;
   int stage = 0;
   for (int it = 0; it < n_tiles; ++it) {
     int kt1 = 0, mk1 = 0, mv1 = 0;
@@ -543,18 +534,18 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
     if (more) issue(kt1, mk1, mv1, next_stage);
 
-    const char *st = lds + stage * kStageBytes;
+    const uint32_t sb = lds_base + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
-      gemm1<true, kSmfmac>(w, st, lo, hf);
+      gemm1<true, kSmfmac>(w, sb, lo, hf);
     else
-      gemm1<false, kSmfmac>(w, st, lo, hf);
+      gemm1<false, kSmfmac>(w, sb, lo, hf);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
-    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c);
+    const float lsum = exp_and_gemm2<kSmfmac>(w, sb_prev, it > 0, prev_sparse_v, lo, hf, c);
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
-    st_prev = st;
+    sb_prev = sb;
     stage = next_stage;
     kt0 = kt1;
     mk0 = mk1;
@@ -563,9 +554,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // GEMM2 of the last tile (its stage is not overwritten after the loop).
   if (n_tiles > 0) {
     uint2 meta[4];
-    load_vmeta(meta, st_prev, prev_sparse_v, lo);
+    load_vmeta(meta, sb_prev, prev_sparse_v, lo);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
+    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, sb_prev, prev_sparse_v, meta, u, lo, hf);
   }
 
   if (!has_task) return;
