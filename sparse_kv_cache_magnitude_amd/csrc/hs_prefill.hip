@@ -98,17 +98,11 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// LDS reads by byte address (the stage base plus a lane offset).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 lds16(uint32_t a) {
-  const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)(size_t)a;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 lds8(uint32_t a) {
-  const u32x2 v = *(__attribute__((address_space(3))) const u32x2 *)(size_t)a;
-  return make_uint2(v.x, v.y);
-}
+// LDS reads. A read address is a stage pointer (a multiple of 32 KB from the 1 KB-aligned LDS
+// array) plus a lane offset with its k-step unit XORed in, plus a constant row-group offset; as the
+// stage pointer has no bits below bit 15, adding it commutes with the XOR.
+__device__ __forceinline__ uint4 lds16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint2 lds8(const char *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 // Two packed 2:4 groups (4 kept values as two dwords, 8 metadata bits) -> 8 dense values.
 __device__ __forceinline__ bf16x8 expand2(uint2 v, uint32_t bits) {
@@ -159,36 +153,33 @@ struct LaneOffsets {
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
 // Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
 template <bool kSparseK, bool kSmfmac>
-__device__ __forceinline__ void gemm1(WaveState &w, uint32_t sb, const LaneOffsets &lo, int hf) {
+__device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     f32x16 acc = zero16();
     if (!kSparseK) {
-      const uint32_t b = sb + lo.kd;
       uint4 k[8];  // all reads issued before the first MFMA that needs them
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16((b ^ (32 * ks)) + T * 8192);
+      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16(st + (lo.kd ^ (32 * ks)) + T * 8192);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         acc = mfma32(as_bf16x8(k[ks]), half8(w.qv[ks >> 1], ks & 1), acc);
     } else {
-      const uint4 meta = lds16(sb + lo.km + T * 512);
+      const uint4 meta = lds16(st + lo.km + T * 512);
       const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
       if (kSmfmac) {
-        const uint32_t b = sb + lo.kn;
         uint4 k[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) k[u] = lds16((b ^ (32 * u)) + T * 4096);
+        for (int u = 0; u < 4; ++u) k[u] = lds16(st + (lo.kn ^ (32 * u)) + T * 4096);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           acc = smfmac32(as_bf16x8(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
       } else {
         // Decompress: the lane's 8-byte half of 16-byte unit ks.
-        const uint32_t b = sb + lo.knd;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const uint32_t bits = (mw[ks >> 1] >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          acc = mfma32(expand2(lds8((b ^ (16 * ks)) + T * 4096), bits),
+          acc = mfma32(expand2(lds8(st + (lo.knd ^ (16 * ks)) + T * 4096), bits),
                        half8(w.qv[ks >> 1], ks & 1), acc);
         }
       }
@@ -203,38 +194,39 @@ __device__ __forceinline__ void gemm1(WaveState &w, uint32_t sb, const LaneOffse
 // lane's tokens 0..7 at group positions {0,1}, index 0x4444), and for a dense tile a second one on
 // tokens 8..15 at positions {2,3} (index 0xEEEE). For a dense tile P^T arrives in the matching
 // token order (tau with bits 1 and 3 exchanged).
-__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, uint32_t sb, bool sparse,
+__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, const char *st, bool sparse,
                                                   const uint2 *meta, int u, const LaneOffsets &lo,
                                                   int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint32_t a = (sparse ? ((sb + lo.vn) ^ (32 * u)) : ((sb + lo.vd) ^ (64 * u))) +
-                       ct * kCtStride;
+    const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
     const uint32_t idx = sparse ? ((u ? meta[ct].y : meta[ct].x) >> (16 * hf)) : 0x4444u;
-    w.o[ct] = smfmac32(as_bf16x8(lds16(a)), w.p[u], idx, w.o[ct]);
-    if (!sparse) w.o[ct] = smfmac32(as_bf16x8(lds16(a ^ 16)), w.p[u], 0xEEEEu, w.o[ct]);
+    w.o[ct] = smfmac32(as_bf16x8(lds16(st + off + ct * kCtStride)), w.p[u], idx, w.o[ct]);
+    if (!sparse)
+      w.o[ct] = smfmac32(as_bf16x8(lds16(st + (off ^ 16) + ct * kCtStride)), w.p[u], 0xEEEEu,
+                         w.o[ct]);
   }
 }
-__device__ __forceinline__ void load_vmeta(uint2 *meta, uint32_t sb, bool sparse,
+__device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
                                            const LaneOffsets &lo) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
-    meta[ct] = sparse ? lds8(sb + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
+    meta[ct] = sparse ? lds8(st + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
 }
 
 // ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
 template <bool kSparseV>
-__device__ __forceinline__ void gemm2_dense_step(WaveState &w, uint32_t sb, const uint2 *meta,
+__device__ __forceinline__ void gemm2_dense_step(WaveState &w, const char *st, const uint2 *meta,
                                                  int ks, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     bf16x8 v;
     if (!kSparseV) {
-      v = as_bf16x8(lds16(((sb + lo.vdd) ^ (32 * ks)) + ct * kCtStride));
+      v = as_bf16x8(lds16(st + (lo.vdd ^ (32 * ks)) + ct * kCtStride));
     } else {
       const uint32_t bits =
           (((ks >> 1) ? meta[ct].y : meta[ct].x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-      v = expand2(lds8(((sb + lo.vnd) ^ (16 * ks)) + ct * kCtStride), bits);
+      v = expand2(lds8(st + (lo.vnd ^ (16 * ks)) + ct * kCtStride), bits);
     }
     w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
   }
@@ -306,16 +298,16 @@ __device__ __forceinline__ void softmax_finish(WaveState &w, bool need, float ls
 }
 
 template <bool kSmfmac>
-__device__ __forceinline__ void gemm2_u(WaveState &w, uint32_t sb, bool sparse,
+__device__ __forceinline__ void gemm2_u(WaveState &w, const char *st, bool sparse,
                                         const uint2 *meta, int u, const LaneOffsets &lo, int hf) {
   if (kSmfmac) {
-    gemm2_smfmac_step(w, sb, sparse, meta, u, lo, hf);
+    gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
   } else if (sparse) {
-    gemm2_dense_step<true>(w, sb, meta, 2 * u, lo, hf);
-    gemm2_dense_step<true>(w, sb, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<true>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<true>(w, st, meta, 2 * u + 1, lo, hf);
   } else {
-    gemm2_dense_step<false>(w, sb, meta, 2 * u, lo, hf);
-    gemm2_dense_step<false>(w, sb, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<false>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<false>(w, st, meta, 2 * u + 1, lo, hf);
   }
 }
 
@@ -323,16 +315,16 @@ __device__ __forceinline__ void gemm2_u(WaveState &w, uint32_t sb, bool sparse,
 // instructions that read P^T of the previous tile are issued first, then the same registers
 // receive P^T of the current tile, 32 tokens at a time.
 template <bool kSmfmac>
-__device__ __forceinline__ float exp_and_gemm2(WaveState &w, uint32_t sb_prev, bool gemm,
+__device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
                                                float c) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
   uint2 meta[4];
-  load_vmeta(meta, sb_prev, gemm && sparse, lo);
+  load_vmeta(meta, st_prev, gemm && sparse, lo);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (gemm) gemm2_u<kSmfmac>(w, sb_prev, sparse, meta, u, lo, hf);
+    if (gemm) gemm2_u<kSmfmac>(w, st_prev, sparse, meta, u, lo, hf);
     softmax_exp(w, 2 * u, c, mc, lsum);
     softmax_exp(w, 2 * u + 1, c, mc, lsum);
   }
@@ -523,7 +515,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
   bool prev_sparse_v = false;
-  uint32_t sb_prev = lds_base;
+  const char *st_prev = lds;
   int stage = 0;
   for (int it = 0; it < n_tiles; ++it) {
     int kt1 = 0, mk1 = 0, mv1 = 0;
@@ -534,18 +526,18 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
     if (more) issue(kt1, mk1, mv1, next_stage);
 
-    const uint32_t sb = lds_base + stage * kStageBytes;
+    const char *st = lds + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
-      gemm1<true, kSmfmac>(w, sb, lo, hf);
+      gemm1<true, kSmfmac>(w, st, lo, hf);
     else
-      gemm1<false, kSmfmac>(w, sb, lo, hf);
+      gemm1<false, kSmfmac>(w, st, lo, hf);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
-    const float lsum = exp_and_gemm2<kSmfmac>(w, sb_prev, it > 0, prev_sparse_v, lo, hf, c);
+    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c);
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
-    sb_prev = sb;
+    st_prev = st;
     stage = next_stage;
     kt0 = kt1;
     mk0 = mk1;
@@ -554,9 +546,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // GEMM2 of the last tile (its stage is not overwritten after the loop).
   if (n_tiles > 0) {
     uint2 meta[4];
-    load_vmeta(meta, sb_prev, prev_sparse_v, lo);
+    load_vmeta(meta, st_prev, prev_sparse_v, lo);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, sb_prev, prev_sparse_v, meta, u, lo, hf);
+    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
   }
 
   if (!has_task) return;
