@@ -108,6 +108,23 @@ def test_prefill_workload_sampled(path):
                  f"{w.name} {path}")
 
 
+def test_prefill_bench_workload_sampled():
+    """Full-size causal prefill at the benchmark's prefill shape (32K tokens, batch 8, 32/8 heads,
+    64-token blocks, 77 pruned / 307 2:4 / 128 dense blocks per head, K outlier channels) on
+    sampled rows, on the SMFMAC path the benchmark times."""
+    w = synth.workload("decode_llama8b_32k_b8")
+    K, V = gu.workload_kv(w.name)
+    Q = synth.make_q(w.seed + 100, w.b, w.hq, w.L, w.D)
+    print(f"[prefill] {w.name} full-size sampled", flush=True)
+    o, lse, cache = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q,
+                                hs.HS_PREFILL_SMFMAC)
+    rows = sample_rows(w.b, w.hq, w.L, 2, 8)
+    ref, ref_lse = oracle.prefill(Dims(w.b, w.hkv, w.L, 128, w.B, *w.counts()),
+                                  gu.cache_to_numpy(cache), Q, rows=rows)
+    assert_close(o.reshape(-1, 128)[rows], ref, lse.reshape(-1)[rows], ref_lse,
+                 f"{w.name} prefill")
+
+
 def test_prefill_paths_agree_and_deterministic():
     rng = np.random.default_rng(21)
     b, hq, hkv, L, B = 1, 8, 2, 1024, 64
