@@ -104,10 +104,15 @@ def prefill_flops(w, map_k, map_v, smfmac=True):
 
 
 def source_digest(*names):
+    """Digest of the code of kernel sources: line comments, trailing blanks and empty lines are
+    dropped, so a comment edit does not void counters taken on the same code."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sparse_kv_cache_magnitude_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_kv_cache_magnitude_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -9,16 +9,18 @@
 // owns one (query head, 32-query tile) task; a workgroup's eight tasks share one KV head (for GQA
 // group size 4: the four query heads of that KV head at two adjacent 32-query tiles), so every K/V
 // tile the workgroup stages serves 256 queries. Query tiles are issued longest-first and the
-// workgroups of one KV head run on one XCD. Two waves per SIMD let one wave's matrix-core work
-// overlap the other's softmax.
+// workgroups of one KV head run on one XCD. Two waves per SIMD cover each other's LDS, barrier
+// and transcendental latencies (the matrix cores and the VALU barely run concurrently on gfx950,
+// so a tile costs about its matrix-core time plus its softmax VALU time).
 //
 // Per visible 64-token KV tile n (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 and
 // v_smfmac_f32_32x32x32_bf16; all accumulators in VGPRs):
 //   staging   three LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) one
 //             tile ahead; one wait for the wave's loads and one barrier per tile. A stage holds
 //             the tile's K and V^T in their stored representation (dense copy, or kept values +
-//             metadata), rows padded by 16 bytes so that the operand reads are free of bank
-//             conflicts with plain immediate offsets.
+//             metadata), rows unit-swizzled so that the operand reads are free of bank
+//             conflicts (layout below). The walk reads its tiles from a list of the
+//             workgroup's visible blocks built at start, so pruned blocks cost nothing.
 //   GEMM1     S^T[64 tok][32 q] = K Q^T (Q stays in registers as the B operand).
 //   softmax   causal mask, column-wise running max (exp2 domain, lazy rescale) and
 //             P^T = exp2(S^T - max) packed to bf16 in registers.
@@ -332,10 +334,10 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev
 }
 
 // ---- staging of one tile -----------------------------------------------------------------------
-// Each region is a whole number of 1 KB loads (64 lanes x 16 B of the padded layout); load q of a
-// region goes to wave q % 8. Pad units receive a copy of a real unit of the same row. Metadata:
-// K (1 KB) by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves
-// 3-6 (block 128, where a tile is half of each channel's metadata row).
+// Each region is a whole number of 1 KB loads (64 lanes x 16 B); load q of a region goes to wave
+// q % 8, so a wave issues two loads for a dense region and one for 2:4 values. Metadata: K (1 KB)
+// by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves 3-6
+// (block 128, where a tile is half of each channel's metadata row).
 
 template <int B, bool kSmfmac>
 __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
