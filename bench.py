@@ -31,6 +31,7 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
+SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress")
 COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
 COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
 
@@ -55,9 +56,12 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="first run a plain device copy of COPY_BYTES (reads and writes a known "
                         "number of bytes: the calibration of rocprofv3's byte counters)")
-    p.add_argument("--suite", action="store_true",
-                   help="instead of the headline step: one JSON line per further workload (16K "
-                        "prefill with both 2:4 paths, 128K decode, the sparsity sweeps)")
+    p.add_argument("--suite", nargs="?", const=",".join(SUITE_PARTS), default=None,
+                   metavar="PARTS",
+                   help="instead of the headline step: one JSON line per further workload; PARTS "
+                        "is a comma list of " + ", ".join(SUITE_PARTS) + " (default: all): 16K "
+                        "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, and the "
+                        "prefill-to-decode re-compression at 32K batch 8")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -240,12 +244,14 @@ def cpu_baseline(w, heads, min_seconds=10.0):
             "decode_s_per_rep": round(per, 4), "compress_s": round(t1 - t0, 3)}
 
 
-def run_suite(reps=7):
+def run_suite(parts=SUITE_PARTS, reps=7):
     """The further measured workloads, one JSON line each: the 16K causal prefill with 128-token
-    blocks on both 2:4 paths, the 128K long-context decode, and the sparsity sweeps (decode and
-    compressor at 64K / batch 16, prefill at 32K / batch 1). Every timing is the median of `reps`
-    HIP-event windows around one call; each decode window follows a 1 GiB read pass (the settled,
-    cold-cache state). Each workload is also run on an all-dense cache (same kernels)."""
+    blocks on both 2:4 paths, the 128K long-context decode, the sparsity sweeps (decode and
+    compressor at 64K / batch 16, prefill at 32K / batch 1) and the re-compression of the 32K
+    batch-8 cache from its prefill counts (K dense) to its decode counts. Every timing is the
+    median of `reps` HIP-event windows around one call; each decode window follows a 1 GiB read
+    pass (the settled, cold-cache state). Workloads are also run on an all-dense cache (same
+    kernels)."""
     import numpy as np
     import torch
     from sparse_kv_cache_magnitude_amd import hierasparse as hs
@@ -290,7 +296,19 @@ def run_suite(reps=7):
     def emit(rec):
         print(json.dumps(rec), flush=True)
 
-    # ---- 16K causal prefill, 128-token blocks, both 2:4 paths ----
+    if "prefill16k" in parts:
+        suite_prefill16k(hs, synth, setup, prefill_time, emit)
+    if "decode128k" in parts:
+        suite_decode128k(hs, synth, setup, decode_time, emit)
+    if "sweeps" in parts:
+        suite_sweeps(hs, synth, setup, decode_time, prefill_time, emit)
+    if "recompress" in parts:
+        suite_recompress(hs, synth, setup, timed, emit, torch)
+    return 0
+
+
+def suite_prefill16k(hs, synth, setup, prefill_time, emit):
+    """16K causal prefill, 128-token blocks, both 2:4 paths, against the all-dense cache."""
     w = synth.workload("prefill_16k_b1_B128")
     K, V, Q, q, shp, cnt, cache, comp = setup(w)
     mk, mv = cache["map_k"].cpu().numpy(), cache["map_v"].cpu().numpy()
@@ -314,7 +332,9 @@ def run_suite(reps=7):
           "compress_us": round(comp * 1e6, 1), "compress_share_of_prefill": round(comp / t_s, 5)})
     del K, V, Q, q, cache, cache0
 
-    # ---- 128K long-context decode ----
+
+def suite_decode128k(hs, synth, setup, decode_time, emit):
+    """128K long-context decode against the all-dense cache."""
     w = synth.workload("decode_128k_b4")
     G = w.hq // w.hkv
     K, V, Q, q, shp, cnt, cache, comp = setup(w)
@@ -329,7 +349,9 @@ def run_suite(reps=7):
           "ideal_speedup_bytes": round(nbytes0 / nbytes, 3), "compress_us": round(comp * 1e6, 1)})
     del K, V, q, cache, cache0
 
-    # ---- sparsity sweeps ----
+
+def suite_sweeps(hs, synth, setup, decode_time, prefill_time, emit):
+    """Sparsity sweeps: decode and compressor at 64K / batch 16, causal prefill at 32K / batch 1."""
     base = None
     for tag in ("0", "50", "62p5", "75"):
         w = synth.workload(f"sweep_decode_64k_b16_s{tag}")
@@ -362,7 +384,33 @@ def run_suite(reps=7):
               "ideal_speedup_executed_flops": round(base[1] / ex, 3),
               "compress_us": round(comp * 1e6, 1), "compress_share_of_prefill": round(comp / t, 5)})
         del K, V, Q, q, cache
-    return 0
+
+
+def suite_recompress(hs, synth, setup, timed, emit, torch):
+    """The 32K batch-8 cache compressed for prefill (K dense, V 2:4) and re-compressed to its
+    decode counts (K and V 2:4). Re-compression = expansion of the cache to dense K, V in the
+    workspace, then the compressor; its bytes by design are the compressed input, the dense
+    intermediate written once and the compressor's own bytes."""
+    w = synth.workload("decode_llama8b_32k_b8")
+    first = (w.n_p, 0, w.n_sv)
+    K, V, Q, q, shp, cnt1, cache1, comp1 = setup(w, first)
+    del Q, q
+    cnt2 = hs.counts(*w.counts())
+    cache2 = hs.alloc_cache(shp, cnt2)
+    ws_c = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt2)
+    comp2 = timed(lambda: hs.hs_compress(shp, cnt2, K, V, cache2, ws_c))
+    ws = hs.alloc_workspace(hs.HS_OP_RECOMPRESS, shp, cnt2)
+    t = timed(lambda: hs.hs_recompress(shp, cnt1, cache1, cnt2, cache2, ws))
+    in_bytes = sum(hs.hs_cache_sizes(shp, cnt1).values())
+    dense = 2 * w.b * w.hkv * w.L * w.D * 2
+    design = in_bytes + dense + compress_bytes(w, hs.hs_cache_sizes(shp, cnt2))
+    emit({"suite": w.name + "_recompress", "from_counts": list(first),
+          "to_counts": list(w.counts()), "recompress_us": round(t * 1e6, 1),
+          "compress_from_dense_us": round(comp2 * 1e6, 1),
+          "compress_prefill_counts_us": round(comp1 * 1e6, 1),
+          "design_bytes": design, "design_gbs": round(design / t / 1e9, 1),
+          "frac_hbm_peak": round(design / t / 1e9 / HBM_PEAK_GBS, 4)})
+    del K, V, cache1, cache2, ws
 
 
 def main():
@@ -370,7 +418,12 @@ def main():
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
     if args.suite:
-        return run_suite()
+        parts = args.suite.split(",")
+        bad = [x for x in parts if x not in SUITE_PARTS]
+        if bad:
+            print(f"unknown suite part(s) {bad}; choose from {SUITE_PARTS}", file=sys.stderr)
+            return 2
+        return run_suite(parts)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -10,6 +10,8 @@
  *                    log-sum-exp combine step and GQA packing.
  *   hs_prefill_attn  [HS] §III-C Algorithm 1 with the mixed dense/sparse dispatch of §III-C2,
  *                    made causal, skipping pruned blocks.
+ *   hs_recompress    [HS] §III, Fig. 3: the cache compressed again with other block counts (e.g.
+ *                    K dense and V 2:4 for prefill, then both 2:4 for decode).
  *
  * Conventions shared by every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
@@ -73,7 +75,8 @@ typedef enum {
   HS_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   HS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hs_workspace_size() */
   HS_ERR_UNSUPPORTED = 6, /* valid request this build does not implement (e.g. flags) */
-  HS_ERR_HIP = 7          /* a HIP launch failed; hs_last_error() has the HIP message */
+  HS_ERR_HIP = 7,         /* a HIP launch failed; hs_last_error() has the HIP message */
+  HS_ERR_OVERLAP = 8      /* hs_recompress: input, output and workspace memory overlap */
 } hs_status;
 
 typedef struct {
@@ -98,7 +101,7 @@ typedef struct {
   size_t map_k, map_v, k_dense, k_nnz, k_meta, v_dense, v_nnz, v_meta;
 } hs_cache_bytes;
 
-enum { HS_OP_COMPRESS = 1, HS_OP_DECODE = 2 };
+enum { HS_OP_COMPRESS = 1, HS_OP_DECODE = 2, HS_OP_RECOMPRESS = 3 };
 
 /* Prefill flags: how 2:4 blocks reach the matrix cores. */
 enum {
@@ -110,11 +113,12 @@ enum {
    GPU needed). A buffer of size 0 may be passed as NULL. */
 hs_status hs_cache_sizes(const hs_shape *shape, const hs_counts *counts, hs_cache_bytes *out);
 
-/* Workspace bytes needed by hs_compress (op = HS_OP_COMPRESS: three 8-byte loss keys per block)
-   or hs_decode_attn (op = HS_OP_DECODE: one uint32 split counter per batch entry, KV head and
+/* Workspace bytes needed by hs_compress (op = HS_OP_COMPRESS: three 8-byte loss keys per block),
+   hs_decode_attn (op = HS_OP_DECODE: one uint32 split counter per batch entry, KV head and
    group of 16 query heads, padded to 256 bytes, then the fp32 partial outputs and log-sum-exps of
-   every split; num_splits = 0 selects the same automatic split count hs_decode_attn uses).
-   Host call. */
+   every split; num_splits = 0 selects the same automatic split count hs_decode_attn uses) or
+   hs_recompress (op = HS_OP_RECOMPRESS: dense K and V [batch][kv_heads][seq_len][head_dim] bf16,
+   then the compressor's keys; the counts only need to be valid). Host call. */
 hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *counts,
                             int32_t num_splits, size_t *bytes);
 
@@ -124,6 +128,17 @@ hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *coun
 hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
                       const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
                       void *stream);
+
+/* Re-compress: 'out' becomes exactly what hs_compress with 'out_counts' produces from the dense
+   K, V that 'in' (compressed with 'in_counts' by hs_compress or hs_recompress) stands for: kept
+   values in place, zeros where a 2:4 group dropped an element and over pruned blocks. A block that
+   is 2:4 or pruned in 'in' has zero loss for that mode, so it is chosen for it first again; dropped
+   values are not recovered. No array of 'in', of 'out' and the workspace may overlap
+   (HS_ERR_OVERLAP). 'ws' is device scratch of hs_workspace_size(HS_OP_RECOMPRESS) bytes.
+   Deterministic. */
+hs_status hs_recompress(const hs_shape *shape, const hs_counts *in_counts, const hs_cache *in,
+                        const hs_counts *out_counts, const hs_cache *out, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /* Decode attention of one new query per (batch entry, query head) over all seq_len cached
    tokens: q [batch][q_heads][head_dim] -> o [batch][q_heads][head_dim] (bf16), and if lse is not

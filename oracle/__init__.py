@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-bas
 this package; the GPU library and its Python binding never import it.
 
 What each function follows is cited in hso.c ("HieraSparse", arXiv 2604.16864v2: Eq. (1),
-Eq. (2a)-(2d), §III-B, §IV-A/B) together with the readings R1-R8 taken where the paper is silent.
+Eq. (2a)-(2d), §III-B, §IV-A/B) together with the readings R1-R8 taken where the paper is silent;
+recompress (§III, Fig. 3) is the composition of unpack and compress (reading R9: re-compression
+works on the values the cache holds, dropped ones being zero).
 Parity is pinned by the tests under tests/ (brute force, closed forms, library routines, identities).
 """
 import ctypes
@@ -115,6 +117,16 @@ def unpack(d: Dims, cache: dict):
     _check(_lib().hso_unpack(ctypes.byref(d.c()), *[_ptr(a) for a in arrs], _ptr(Kt), _ptr(Vt),
                              _ptr(vis)))
     return Kt, Vt, vis
+
+
+def recompress(d_in: Dims, cache: dict, d_out: Dims) -> dict:
+    """Re-compression with other block counts ([HS] §III, Fig. 3: one compression for prefill,
+    another for decode): the compressor applied to the dense tensors the compressed cache stands
+    for. d_in and d_out differ only in their counts."""
+    assert (d_in.b, d_in.hkv, d_in.L, d_in.D, d_in.B) == (d_out.b, d_out.hkv, d_out.L, d_out.D,
+                                                           d_out.B)
+    Kt, Vt, _ = unpack(d_in, cache)
+    return compress(d_out, Kt, Vt)
 
 
 def attention(Q, Kt, Vt, visible, B: int, causal: bool, scale: float = 0.0, rows=None):

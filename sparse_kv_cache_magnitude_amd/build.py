@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhierasparse.so")
-SOURCES = ["hs_api.hip", "hs_compress.hip", "hs_decode.hip", "hs_prefill.hip"]
+SOURCES = ["hs_api.hip", "hs_compress.hip", "hs_decode.hip", "hs_prefill.hip",
+           "hs_recompress.hip"]
 ARCH = "gfx950"
 
 

@@ -136,6 +136,26 @@ size_t decode_ws_bytes(const hs::Dims &d, int splits) {
 
 size_t compress_ws_bytes(const hs::Dims &d) { return (size_t)d.b * d.hkv * d.nb * 3 * sizeof(uint64_t); }
 
+// Byte ranges [p, p + n) of a cache's eight arrays (empty arrays have n = 0).
+struct Ranges {
+  const char *p[8];
+  size_t n[8];
+};
+Ranges cache_ranges(const hs_cache *c, const hs::Dims &d) {
+  const hs_cache_bytes b = cache_bytes(d);
+  return Ranges{{(const char *)c->map_k, (const char *)c->map_v, (const char *)c->k_dense,
+                 (const char *)c->k_nnz, (const char *)c->k_meta, (const char *)c->v_dense,
+                 (const char *)c->v_nnz, (const char *)c->v_meta},
+                {b.map_k, b.map_k, b.k_dense, b.k_nnz, b.k_meta, b.v_dense, b.v_nnz, b.v_meta}};
+}
+bool overlap(const char *a, size_t na, const char *b, size_t nb) {
+  return na && nb && a < b + nb && b < a + na;
+}
+
+// Re-compression workspace: dense K and V of the shape, then the compressor's keys.
+size_t dense_bytes(const hs::Dims &d) { return (size_t)d.b * d.hkv * d.L * d.D * sizeof(uint16_t); }
+size_t recompress_ws_bytes(const hs::Dims &d) { return 2 * dense_bytes(d) + compress_ws_bytes(d); }
+
 float scale_log2(float softmax_scale, int D) {
   float s = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   return s * 1.4426950408889634f;
@@ -161,6 +181,8 @@ HS_API hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_count
   if (!bytes) return fail(HS_ERR_NULL, "bytes is NULL");
   if (op == HS_OP_COMPRESS) {
     *bytes = compress_ws_bytes(d);
+  } else if (op == HS_OP_RECOMPRESS) {
+    *bytes = recompress_ws_bytes(d);
   } else if (op == HS_OP_DECODE) {
     if (num_splits < 0 || num_splits > 512)
       return fail(HS_ERR_SHAPE, "num_splits must be in 0..512 (got %d)", num_splits);
@@ -186,6 +208,39 @@ HS_API hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, con
   if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
   hipError_t e = hs::launch_compress(d, k, v, c, (uint64_t *)ws, (hipStream_t)stream);
   if (e != hipSuccess) return fail(HS_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+HS_API hs_status hs_recompress(const hs_shape *shape, const hs_counts *in_counts,
+                               const hs_cache *in, const hs_counts *out_counts,
+                               const hs_cache *out, void *ws, size_t ws_bytes, void *stream) {
+  hs::Dims din, dout;
+  hs::CacheView cin, cout;
+  hs_status st = make_dims(shape, in_counts, &din);
+  if (st) return st;
+  if ((st = make_dims(shape, out_counts, &dout))) return st;
+  if ((st = check_cache(in, din, &cin))) return st;
+  if ((st = check_cache(out, dout, &cout))) return st;
+  const size_t need = recompress_ws_bytes(dout);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                ws ? "" : ", NULL");
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const Ranges ri = cache_ranges(in, din), ro = cache_ranges(out, dout);
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(ri.p[i], ri.n[i], (const char *)ws, need) ||
+        overlap(ro.p[i], ro.n[i], (const char *)ws, need))
+      return fail(HS_ERR_OVERLAP, "workspace overlaps a cache array");
+    for (int j = 0; j < 8; ++j)
+      if (overlap(ri.p[i], ri.n[i], ro.p[j], ro.n[j]))
+        return fail(HS_ERR_OVERLAP, "input and output caches overlap");
+  }
+  uint16_t *kd = (uint16_t *)ws;
+  uint16_t *vd = kd + dense_bytes(dout) / sizeof(uint16_t);
+  uint64_t *keys = (uint64_t *)(vd + dense_bytes(dout) / sizeof(uint16_t));
+  hipError_t e = hs::launch_unpack(din, cin, kd, vd, (hipStream_t)stream);
+  if (e == hipSuccess) e = hs::launch_compress(dout, kd, vd, cout, keys, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "recompress launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -245,6 +300,7 @@ HS_API const char *hs_status_string(hs_status s) {
     case HS_ERR_WORKSPACE: return "workspace missing or too small";
     case HS_ERR_UNSUPPORTED: return "unsupported request";
     case HS_ERR_HIP: return "HIP launch error";
+    case HS_ERR_OVERLAP: return "overlapping buffers";
   }
   return "unknown status";
 }

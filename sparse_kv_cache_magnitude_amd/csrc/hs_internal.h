@@ -33,4 +33,9 @@ hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, u
 hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                           float *lse, float scale_log2, bool smfmac, hipStream_t stream);
 
+// Dense stand-ins of a compressed cache: K, V [b][hkv][L][D] with kept values in place and zeros
+// elsewhere (hs_recompress.hip).
+hipError_t launch_unpack(const Dims &d, const CacheView &c, uint16_t *k_out, uint16_t *v_out,
+                         hipStream_t stream);
+
 }  // namespace hs

@@ -58,6 +58,9 @@ def test_workspace_sizes():
         # (head_dim) and log-sum-exp per (batch, query head, split)
         assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) == 256 + 2 * 8 * s * (128 + 1) * 4
     assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, 0) > 0
+    # dense K and V bf16 of the whole shape, then the compressor's keys
+    assert hs.hs_workspace_size(hs.HS_OP_RECOMPRESS, shp, cnt) == \
+        2 * (2 * 2 * 1024 * 128 * 2) + 2 * 2 * 16 * 3 * 8
 
 
 def _status(call):
@@ -111,6 +114,12 @@ def _raise(st):
 def _compress(shp, cnt, k, v, cache, ws, ws_bytes):
     _raise(hs.lib().hs_compress(ctypes.byref(shp), ctypes.byref(cnt), k, v,
                                 ctypes.byref(_cache_struct(cache)), ws, ws_bytes, None))
+
+
+def _recompress(shp, cin, cache_in, cout, cache_out, ws, ws_bytes):
+    _raise(hs.lib().hs_recompress(ctypes.byref(shp), ctypes.byref(cin),
+                                  ctypes.byref(_cache_struct(cache_in)), ctypes.byref(cout),
+                                  ctypes.byref(_cache_struct(cache_out)), ws, ws_bytes, None))
 
 
 def _decode(shp, cnt, cache, q, o, lse, splits, ws, ws_bytes):
@@ -168,6 +177,38 @@ def test_workspace_checks():
         == hs.HS_ERR_SHAPE
 
 
+def _disjoint_caches():
+    """Placeholder input and output caches whose arrays are far apart, and a workspace address."""
+    cin = {f: (1 << 40) + (i << 32) for i, f in enumerate(hs.CACHE_FIELDS)}
+    cout = {f: (1 << 41) + (i << 32) for i, f in enumerate(hs.CACHE_FIELDS)}
+    return cin, cout, 1 << 42
+
+
+def test_recompress_validation():
+    cin, cout, ws = _disjoint_caches()
+    c2 = hs.counts(2, 6, 6)
+    need = hs.hs_workspace_size(hs.HS_OP_RECOMPRESS, SHP, c2)
+    call = lambda shp=SHP, a=CNT, ca=cin, b=c2, cb=cout, w=ws, n=need: \
+        _status(lambda: _recompress(shp, a, ca, b, cb, w, n))
+    assert call(n=need - 1) == hs.HS_ERR_WORKSPACE
+    assert call(w=None) == hs.HS_ERR_WORKSPACE
+    assert call(w=ws + 8) == hs.HS_ERR_ALIGN
+    assert call(a=hs.counts(10, 7, 0)) == hs.HS_ERR_COUNTS
+    assert call(b=hs.counts(0, 17, 0)) == hs.HS_ERR_COUNTS
+    assert call(shp=hs.shape(1, 4, 1, 1000, 128, 64)) == hs.HS_ERR_SHAPE
+    for f in hs.CACHE_FIELDS:
+        assert call(ca=dict(cin, **{f: None})) == hs.HS_ERR_NULL
+        assert call(cb=dict(cout, **{f: None})) == hs.HS_ERR_NULL
+        assert call(cb=dict(cout, **{f: cout[f] + 8})) == hs.HS_ERR_ALIGN
+    # any shared byte between an input array, an output array and the workspace is refused
+    for f in hs.CACHE_FIELDS:
+        for g in hs.CACHE_FIELDS:
+            assert call(cb=dict(cout, **{g: cin[f] + 16})) == hs.HS_ERR_OVERLAP, (f, g)
+        assert call(w=cin[f]) == hs.HS_ERR_OVERLAP
+        assert call(w=cout[f] - need + 16) == hs.HS_ERR_OVERLAP
+    assert "overlap" in hs.hs_last_error()
+
+
 def test_unknown_flags_and_ops():
     cache = {f: FAKE for f in hs.CACHE_FIELDS}
     assert _status(lambda: _prefill(SHP, CNT, cache, FAKE, FAKE, None, 7)) == hs.HS_ERR_UNSUPPORTED
@@ -175,5 +216,5 @@ def test_unknown_flags_and_ops():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert hs.hs_status_string(code) not in ("", "unknown status")

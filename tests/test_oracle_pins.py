@@ -174,6 +174,56 @@ def test_round_trip_and_map_is_a_bijection():
     assert (Kt2 == Kt).all() and (Vt2 == Vt).all() and (vis2 == vis).all()
 
 
+# ------------------------------------------------------------------------------------------------
+# Re-compression ([HS] §III, Fig. 3): compress(unpack(cache), counts')
+
+def _same_cache(a, b):
+    for k in oracle.POOLS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("maker", [tie_heavy, normal])
+@pytest.mark.parametrize("counts", [(0, 3, 5), (2, 3, 4), (3, 5, 0), (0, 8, 8), (8, 0, 0)])
+def test_recompress_identities(maker, counts):
+    d = Dims(b=2, hkv=2, L=256, D=32, B=32, n_p=0, n_sk=0, n_sv=0)
+    K = maker((d.b, d.hkv, d.L, d.D), 21)
+    V = maker((d.b, d.hkv, d.L, d.D), 22)
+    dc = Dims(d.b, d.hkv, d.L, d.D, d.B, *counts)
+    want = oracle.compress(dc, K, V)
+    # an all-dense cache holds every value: re-compressing it is compressing from scratch
+    _same_cache(oracle.recompress(d, oracle.compress(d, K, V), dc), want)
+    # a 2:4 or pruned block has zero loss for its own mode, so the same counts change nothing
+    _same_cache(oracle.recompress(dc, want, dc), want)
+    # the prefill-to-decode phase change (one tensor 2:4 first, then both) loses nothing against
+    # compressing the original values with the decode counts
+    n_p, n_sk, n_sv = counts
+    for first in ((n_p, 0, n_sv), (n_p, n_sk, 0)):
+        d1 = Dims(d.b, d.hkv, d.L, d.D, d.B, *first)
+        _same_cache(oracle.recompress(d1, oracle.compress(d1, K, V), dc), want)
+    # towards dense nothing is recovered: the cache stands for the same tensors as before
+    d0 = Dims(d.b, d.hkv, d.L, d.D, d.B, n_p, 0, 0)
+    back = oracle.recompress(dc, want, d0)
+    Kt, Vt, vis, _, _ = pinlib.decode_cache(d.b, d.hkv, d.L, d.D, d.B, want)
+    Kt0, Vt0, vis0, keepK0, keepV0 = pinlib.decode_cache(d.b, d.hkv, d.L, d.D, d.B, back)
+    assert (Kt0 == Kt).all() and (Vt0 == Vt).all() and (vis0 == vis).all()
+    assert (back["map_k"] >= 0).all() and (back["map_v"] >= 0).all()
+
+
+def test_recompress_changes_modes_by_the_held_values():
+    # a block whose 2:4 loss was high in the original still ranks by what the cache holds
+    d = Dims(b=1, hkv=1, L=128, D=16, B=16, n_p=0, n_sk=0, n_sv=0)
+    K = normal((1, 1, d.L, d.D), 31)
+    V = normal((1, 1, d.L, d.D), 32)
+    K[..., 16:32, :] = synth.bf16_bits(np.float32(40.0) * np.ones((16, 16), np.float32))
+    d_first = Dims(1, 1, d.L, d.D, d.B, 0, 3, 0)
+    first = oracle.compress(d_first, K, V)
+    # block 1 holds large equal values: its K 2:4 loss is the largest, so it stays dense
+    assert first["map_k"][1] > 0
+    again = oracle.recompress(d_first, first, Dims(1, 1, d.L, d.D, d.B, 0, 4, 0))
+    # the three 2:4 blocks keep their mode (zero loss) and one more is chosen among the rest
+    assert ((first["map_k"] < 0) <= (again["map_k"] < 0)).all() and (again["map_k"] < 0).sum() == 4
+
+
 def test_rejects_out_of_range_inputs():
     d = Dims(b=1, hkv=1, L=16, D=16, B=16, n_p=0, n_sk=1, n_sv=0)
     K = np.zeros((1, 1, 16, 16), np.uint16)
