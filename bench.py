@@ -31,7 +31,7 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
-SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress")
+SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked")
 COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
 COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
 
@@ -60,8 +60,9 @@ def parse():
                    metavar="PARTS",
                    help="instead of the headline step: one JSON line per further workload; PARTS "
                         "is a comma list of " + ", ".join(SUITE_PARTS) + " (default: all): 16K "
-                        "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, and the "
-                        "prefill-to-decode re-compression at 32K batch 8")
+                        "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, the "
+                        "prefill-to-decode re-compression and the caller-mask compressor at 32K "
+                        "batch 8")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -304,6 +305,8 @@ def run_suite(parts=SUITE_PARTS, reps=7):
         suite_sweeps(hs, synth, setup, decode_time, prefill_time, emit)
     if "recompress" in parts:
         suite_recompress(hs, synth, setup, timed, emit, torch)
+    if "masked" in parts:
+        suite_masked(hs, synth, setup, timed, emit, torch)
     return 0
 
 
@@ -412,6 +415,34 @@ def suite_recompress(hs, synth, setup, timed, emit, torch):
           "frac_hbm_peak": round(design / t / 1e9 / HBM_PEAK_GBS, 4)})
     del K, V, cache1, cache2, ws
 
+
+def suite_masked(hs, synth, setup, timed, emit, torch):
+    """The caller-mask compressor on the 32K batch-8 shape: random block masks at the workload's
+    counts, random 2:4 element masks applied in the 2:4 blocks (drawn on the host), against the
+    magnitude compressor on the same tensors. Algorithmic bytes: K and V of the blocks that are not
+    pruned, both mode arrays, and the compressed cache written."""
+    import numpy as np
+    w = synth.workload("decode_llama8b_32k_b8")
+    K, V, Q, q, shp, cnt, cache, comp = setup(w)
+    del Q, q
+    mk, mv = synth.random_modes(41, w.b, w.hkv, w.nb, *w.counts())
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    Kh = K.view(torch.int16).cpu().numpy().view(np.uint16)
+    Vh = V.view(torch.int16).cpu().numpy().view(np.uint16)
+    Km = dev(synth.random_element_mask(42, Kh, mk, w.B, False).view(np.int16))
+    Vm = dev(synth.random_element_mask(43, Vh, mv, w.B, True).view(np.int16))
+    del Kh, Vh
+    mkd, mvd = dev(mk), dev(mv)
+    status = torch.empty(w.b * w.hkv, dtype=torch.int32, device="cuda")
+    t = timed(lambda: hs.hs_compress_masked(shp, cnt, Km, Vm, mkd, mvd, cache, status))
+    assert int(status.abs().sum()) == 0
+    kept = w.nb - w.n_p
+    nbytes = (2 * w.b * w.hkv * kept * w.B * w.D * 2 + 2 * mk.size
+              + sum(hs.hs_cache_sizes(shp, cnt).values()))
+    emit({"suite": w.name + "_masked", "masked_compress_us": round(t * 1e6, 1),
+          "magnitude_compress_us": round(comp * 1e6, 1), "bytes": nbytes,
+          "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+    del K, V, Km, Vm, cache
 
 def main():
     args = parse()

@@ -12,6 +12,8 @@
  *                    made causal, skipping pruned blocks.
  *   hs_recompress    [HS] §III, Fig. 3: the cache compressed again with other block counts (e.g.
  *                    K dense and V 2:4 for prefill, then both 2:4 for decode).
+ *   hs_compress_masked  [HS] §III-A cache pruner fed by any pruning algorithm's block-level and
+ *                    element-level masks + §IV-B generic compression kernel.
  *
  * Conventions shared by every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
@@ -128,6 +130,24 @@ hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *coun
 hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
                       const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
                       void *stream);
+
+/* Compress with the caller's masks instead of the magnitude ranking. mode_k, mode_v: uint8
+   [batch][kv_heads][nb] device arrays, one per block: 0 = pruned, 1 = dense, 2 = 2:4. The element
+   mask must already be applied to k and v: in every group of four of a 2:4 block at most two
+   values are non-zero (bf16 +0 and -0 count as zero). Such a group is stored as its non-zero
+   values and their positions, padded with the lowest-position zeros to exactly two; a group with
+   more non-zeros keeps its two largest |x| (lower position on ties), as hs_compress does.
+   Per (batch entry, KV head) the modes must match 'counts': n_pruned blocks pruned for both K and
+   V, n_sparse_k K blocks and n_sparse_v V blocks 2:4, no byte above 2. A head that does not is
+   rejected: its maps are written as all pruned and its pool slots are left as they were.
+   head_status (optional, int32 [batch][kv_heads] device array, NULL = not wanted) receives 0 for
+   an accepted head, else the OR of 1 (a mode byte above 2), 2 (K and V disagree on a pruned
+   block) and 4 (the numbers of K bytes equal to 0, K bytes equal to 2 and V bytes equal to 2
+   are not n_pruned, n_sparse_k and n_sparse_v). Pool layout and slot order are those of
+   hs_compress. No workspace. Deterministic. */
+hs_status hs_compress_masked(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
+                             const uint16_t *v, const uint8_t *mode_k, const uint8_t *mode_v,
+                             const hs_cache *out, int32_t *head_status, void *stream);
 
 /* Re-compress: 'out' becomes exactly what hs_compress with 'out_counts' produces from the dense
    K, V that 'in' (compressed with 'in_counts' by hs_compress or hs_recompress) stands for: kept

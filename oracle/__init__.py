@@ -5,8 +5,8 @@ this package; the GPU library and its Python binding never import it.
 
 What each function follows is cited in hso.c ("HieraSparse", arXiv 2604.16864v2: Eq. (1),
 Eq. (2a)-(2d), §III-B, §IV-A/B) together with the readings R1-R8 taken where the paper is silent;
-recompress (§III, Fig. 3) is the composition of unpack and compress (reading R9: re-compression
-works on the values the cache holds, dropped ones being zero).
+recompress (§III, Fig. 3) is the composition of unpack and compress (R9), compress_masked the
+generic compressor fed by caller masks (§III-A, §IV-B; R10).
 Parity is pinned by the tests under tests/ (brute force, closed forms, library routines, identities).
 """
 import ctypes
@@ -37,9 +37,11 @@ def _lib():
         lib.hso_pool_elems.argtypes = [ctypes.POINTER(_Dims), P]
         lib.hso_compress.argtypes = [ctypes.POINTER(_Dims)] + [P] * 12
         lib.hso_unpack.argtypes = [ctypes.POINTER(_Dims)] + [P] * 11
+        lib.hso_compress_masked.argtypes = [ctypes.POINTER(_Dims)] + [P] * 13
         lib.hso_attention.argtypes = [ctypes.c_int] * 8 + [P] * 4 + [ctypes.c_double,
                                                                       ctypes.c_int64, P, P, P]
-        for f in (lib.hso_pool_elems, lib.hso_compress, lib.hso_unpack, lib.hso_attention):
+        for f in (lib.hso_pool_elems, lib.hso_compress, lib.hso_unpack, lib.hso_attention,
+                  lib.hso_compress_masked):
             f.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -104,6 +106,27 @@ def compress(d: Dims, K: np.ndarray, V: np.ndarray, with_loss: bool = False) -> 
     out["keys"] = keys
     if with_loss:
         out["loss"] = loss
+    return out
+
+
+def compress_masked(d: Dims, K: np.ndarray, V: np.ndarray, mode_k: np.ndarray,
+                    mode_v: np.ndarray) -> dict:
+    """Compression with caller masks ([HS] §III-A cache pruner, §IV-B generic kernel; hso.c R10).
+    K, V [b][Hkv][L][D] bf16 bits with the element mask applied; mode_k, mode_v [b][Hkv][nb]
+    uint8 (0 pruned, 1 dense, 2 2:4). Returns the maps, the six pools (zero where nothing is
+    written) and 'head_status' [b][Hkv] int32."""
+    K = np.ascontiguousarray(K, dtype=np.uint16)
+    V = np.ascontiguousarray(V, dtype=np.uint16)
+    assert K.shape == V.shape == (d.b, d.hkv, d.L, d.D)
+    mk = np.ascontiguousarray(mode_k, dtype=np.uint8)
+    mv = np.ascontiguousarray(mode_v, dtype=np.uint8)
+    assert mk.shape == mv.shape == (d.b, d.hkv, d.nb)
+    n = pool_elems(d)
+    out = {k: np.zeros(n[k], np.int32 if k.startswith("map") else np.uint16) for k in POOLS}
+    status = np.zeros((d.b, d.hkv), np.int32)
+    _check(_lib().hso_compress_masked(ctypes.byref(d.c()), _ptr(K), _ptr(V), _ptr(mk), _ptr(mv),
+                                      *[_ptr(out[k]) for k in POOLS], _ptr(status)))
+    out["head_status"] = status
     return out
 
 

@@ -35,6 +35,14 @@
  *   R7 decode: the single query attends every visible cached token; prefill: query position i
  *      attends visible tokens t <= i (causal).
  *   R8 GQA: query head hq reads KV head hq / (Hq / Hkv).
+ *   R9 re-compression ([HS] §III, Fig. 3) compresses what the cache holds: kept values in place,
+ *      zeros for dropped elements and pruned blocks (oracle/__init__.py: recompress).
+ *   R10 generic compression with caller masks ([HS] §III-A cache pruner, §IV-B generic kernel):
+ *      a 2:4 group of the pre-masked input is stored as its non-zero elements (+0 and -0 are
+ *      zero) in position order, padded with the lowest-position zeros to exactly two; a group
+ *      with more than two non-zeros violates the mask and falls back to R1's top-2. A (batch,
+ *      KV head) whose block modes do not match the pool counts is rejected: all-pruned map, no
+ *      pool writes, a status bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -123,6 +131,23 @@ static void keep_two(const uint16_t x[4], int *i0, int *i1) {
   *i0 = order[0] < order[1] ? order[0] : order[1];
   *i1 = order[0] < order[1] ? order[1] : order[0];
 }
+
+/* R10: the generic kernel's selection for a group the caller's element mask already thinned. */
+static void keep_nonzero(const uint16_t x[4], int *i0, int *i1) {
+  int pos[4], n = 0;
+  for (int j = 0; j < 4; ++j)
+    if (x[j] & 0x7FFFu) pos[n++] = j;
+  if (n > 2) {
+    keep_two(x, i0, i1);
+    return;
+  }
+  for (int j = 0; j < 4 && n < 2; ++j)
+    if (!(x[j] & 0x7FFFu)) pos[n++] = j;
+  *i0 = pos[0] < pos[1] ? pos[0] : pos[1];
+  *i1 = pos[0] < pos[1] ? pos[1] : pos[0];
+}
+
+typedef void (*select_fn)(const uint16_t x[4], int *i0, int *i1);
 
 /* The four elements of group g of block i, for K (4 consecutive channels of one token, row = the
    token within the block) or V (4 consecutive tokens of one channel, row = the channel). */
@@ -218,18 +243,65 @@ static void block_modes(const hso_dims *d, const uint64_t *keys, int *mode_k, in
 /* ------------------------------------------------------------------------------------------ */
 /* Compressor: [HS] §III-B memory pools and index map, §IV-A/B packing.                        */
 
-/* One 2:4 row: 'groups' groups gathered by gather_group -> nnz (2 per group), meta (1 per 4). */
+/* One 2:4 row: 'groups' groups gathered by gather_group -> nnz (2 per group), meta (1 per 4);
+   'select' picks the two stored positions of a group. */
 static void pack_row(const uint16_t *X, int is_v, const hso_dims *d, int i, int row, int groups,
-                     uint16_t *nnz, uint16_t *meta) {
+                     select_fn select, uint16_t *nnz, uint16_t *meta) {
   for (int w = 0; w < groups / 4; ++w) meta[w] = 0;
   for (int g = 0; g < groups; ++g) {
     uint16_t x[4];
     int i0, i1;
     gather_group(X, is_v, d->L, d->D, d->B, i, row, g, x);
-    keep_two(x, &i0, &i1);
+    select(x, &i0, &i1);
     nnz[2 * g] = x[i0];
     nnz[2 * g + 1] = x[i1];
     meta[g / 4] |= (uint16_t)((i0 | (i1 << 2)) << (4 * (g % 4)));
+  }
+}
+
+/* [HS] §III-B: the pools and map entries of one (batch, KV head) from its block modes; walks the
+   blocks in order with one dense and one sparse counter per tensor. Each head owns a contiguous
+   range of each pool, so the counters start at head * count. */
+static void write_head(const hso_dims *d, int64_t hd, const uint16_t *Kh, const uint16_t *Vh,
+                       const int *mode_k, const int *mode_v, select_fn select, int32_t *map_k,
+                       int32_t *map_v, uint16_t *k_dense, uint16_t *k_nnz, uint16_t *k_meta,
+                       uint16_t *v_dense, uint16_t *v_nnz, uint16_t *v_meta) {
+  const int nb = d->L / d->B, B = d->B, D = d->D;
+  const int ndk = nb - d->n_p - d->n_sk, ndv = nb - d->n_p - d->n_sv;
+  const int64_t BD = (int64_t)B * D;
+  int64_t dk = hd * ndk, sk = hd * d->n_sk, dv = hd * ndv, sv = hd * d->n_sv;
+  for (int i = 0; i < nb; ++i) {
+    int32_t *mk = &map_k[hd * nb + i], *mv = &map_v[hd * nb + i];
+    /* K: 2:4 along head_dim, one row per token. */
+    if (mode_k[i] == 0) {
+      *mk = 0;
+    } else if (mode_k[i] == 1) {
+      memcpy(k_dense + dk * BD, Kh + (int64_t)i * BD, sizeof(uint16_t) * BD);
+      *mk = (int32_t)(dk + 1);
+      ++dk;
+    } else {
+      for (int t = 0; t < B; ++t)
+        pack_row(Kh, 0, d, i, t, D / 4, select, k_nnz + sk * BD / 2 + (int64_t)t * D / 2,
+                 k_meta + sk * BD / 16 + (int64_t)t * D / 16);
+      *mk = (int32_t)-(sk + 1);
+      ++sk;
+    }
+    /* V: 2:4 along tokens, one row per channel; the dense copy is stored channel-major. */
+    if (mode_v[i] == 0) {
+      *mv = 0;
+    } else if (mode_v[i] == 1) {
+      for (int c = 0; c < D; ++c)
+        for (int t = 0; t < B; ++t)
+          v_dense[dv * BD + (int64_t)c * B + t] = Vh[(int64_t)(i * B + t) * D + c];
+      *mv = (int32_t)(dv + 1);
+      ++dv;
+    } else {
+      for (int c = 0; c < D; ++c)
+        pack_row(Vh, 1, d, i, c, B / 4, select, v_nnz + sv * BD / 2 + (int64_t)c * B / 2,
+                 v_meta + sv * BD / 16 + (int64_t)c * B / 16);
+      *mv = (int32_t)-(sv + 1);
+      ++sv;
+    }
   }
 }
 
@@ -248,10 +320,7 @@ int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_
   for (int64_t e = 0; e < heads * per_head; ++e)
     if (!bf16_in_range(K[e]) || !bf16_in_range(V[e])) return HSO_ERR_VALUE;
 
-  const int nb = d->L / d->B, B = d->B, D = d->D;
-  const int ndk = nb - d->n_p - d->n_sk, ndv = nb - d->n_p - d->n_sv;
-  const int64_t BD = (int64_t)B * D;
-
+  const int nb = d->L / d->B;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t hd = 0; hd < heads; ++hd) {
     const uint16_t *Kh = K + hd * per_head, *Vh = V + hd * per_head;
@@ -262,47 +331,57 @@ int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_
     block_keys(d, Kh, Vh, keys, loss);
     if (keys_out) memcpy(keys_out + hd * 3 * nb, keys, sizeof(uint64_t) * 3 * nb);
     block_modes(d, keys, mode_k, mode_v, scratch);
-
-    /* [HS] §III-B: walk the blocks in order with one dense and one sparse counter per tensor.
-       Each head owns a contiguous range of each pool, so the counters start at head * count. */
-    int64_t dk = hd * ndk, sk = hd * d->n_sk, dv = hd * ndv, sv = hd * d->n_sv;
-    for (int i = 0; i < nb; ++i) {
-      int32_t *mk = &map_k[hd * nb + i], *mv = &map_v[hd * nb + i];
-      /* K: 2:4 along head_dim, one row per token. */
-      if (mode_k[i] == 0) {
-        *mk = 0;
-      } else if (mode_k[i] == 1) {
-        memcpy(k_dense + dk * BD, Kh + (int64_t)i * BD, sizeof(uint16_t) * BD);
-        *mk = (int32_t)(dk + 1);
-        ++dk;
-      } else {
-        for (int t = 0; t < B; ++t)
-          pack_row(Kh, 0, d, i, t, D / 4, k_nnz + sk * BD / 2 + (int64_t)t * D / 2,
-                   k_meta + sk * BD / 16 + (int64_t)t * D / 16);
-        *mk = (int32_t)-(sk + 1);
-        ++sk;
-      }
-      /* V: 2:4 along tokens, one row per channel; the dense copy is stored channel-major. */
-      if (mode_v[i] == 0) {
-        *mv = 0;
-      } else if (mode_v[i] == 1) {
-        for (int c = 0; c < D; ++c)
-          for (int t = 0; t < B; ++t)
-            v_dense[dv * BD + (int64_t)c * B + t] = Vh[(int64_t)(i * B + t) * D + c];
-        *mv = (int32_t)(dv + 1);
-        ++dv;
-      } else {
-        for (int c = 0; c < D; ++c)
-          pack_row(Vh, 1, d, i, c, B / 4, v_nnz + sv * BD / 2 + (int64_t)c * B / 2,
-                   v_meta + sv * BD / 16 + (int64_t)c * B / 16);
-        *mv = (int32_t)-(sv + 1);
-        ++sv;
-      }
-    }
+    write_head(d, hd, Kh, Vh, mode_k, mode_v, keep_two, map_k, map_v, k_dense, k_nnz, k_meta,
+               v_dense, v_nnz, v_meta);
     free(keys);
     free(mode_k);
     free(mode_v);
     free(scratch);
+  }
+  return HSO_OK;
+}
+
+/*
+ * hso_compress_masked: compression with the caller's masks ([HS] §III-A cache pruner, §IV-B
+ * generic kernel; R10). mode_k, mode_v: [b][hkv][nb] bytes, 0 pruned / 1 dense / 2 2:4. K, V
+ * carry the element mask already. head_status [b][hkv] receives 0, or the OR of 1 (a mode above
+ * 2), 2 (K and V disagree on a pruned block), 4 (counts differ from d's); a rejected head gets an
+ * all-pruned map and no pool writes. Returns HSO_ERR_VALUE if an input is not finite.
+ */
+int hso_compress_masked(const hso_dims *d, const uint16_t *K, const uint16_t *V,
+                        const uint8_t *mode_k, const uint8_t *mode_v, int32_t *map_k,
+                        int32_t *map_v, uint16_t *k_dense, uint16_t *k_nnz, uint16_t *k_meta,
+                        uint16_t *v_dense, uint16_t *v_nnz, uint16_t *v_meta,
+                        int32_t *head_status) {
+  int rc = dims_check(d);
+  if (rc) return rc;
+  const int64_t heads = (int64_t)d->b * d->hkv, per_head = (int64_t)d->L * d->D;
+  for (int64_t e = 0; e < heads * per_head; ++e)
+    if ((K[e] & 0x7F80u) == 0x7F80u || (V[e] & 0x7F80u) == 0x7F80u) return HSO_ERR_VALUE;
+
+  const int nb = d->L / d->B;
+  for (int64_t hd = 0; hd < heads; ++hd) {
+    const uint8_t *mk = mode_k + hd * nb, *mv = mode_v + hd * nb;
+    int status = 0, n_p = 0, n_sk = 0, n_sv = 0;
+    for (int i = 0; i < nb; ++i) {
+      if (mk[i] > 2 || mv[i] > 2) status |= 1;
+      if ((mk[i] == 0) != (mv[i] == 0)) status |= 2;
+      n_p += mk[i] == 0;
+      n_sk += mk[i] == 2;
+      n_sv += mv[i] == 2;
+    }
+    if (n_p != d->n_p || n_sk != d->n_sk || n_sv != d->n_sv) status |= 4;
+    head_status[hd] = status;
+    if (status) {
+      for (int i = 0; i < nb; ++i) map_k[hd * nb + i] = map_v[hd * nb + i] = 0;
+      continue;
+    }
+    int *ik = (int *)malloc(sizeof(int) * nb), *iv = (int *)malloc(sizeof(int) * nb);
+    for (int i = 0; i < nb; ++i) { ik[i] = mk[i]; iv[i] = mv[i]; }
+    write_head(d, hd, K + hd * per_head, V + hd * per_head, ik, iv, keep_nonzero, map_k, map_v,
+               k_dense, k_nnz, k_meta, v_dense, v_nnz, v_meta);
+    free(ik);
+    free(iv);
   }
   return HSO_OK;
 }

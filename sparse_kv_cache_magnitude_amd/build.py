@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhierasparse.so")
 SOURCES = ["hs_api.hip", "hs_compress.hip", "hs_decode.hip", "hs_prefill.hip",
-           "hs_recompress.hip"]
+           "hs_recompress.hip", "hs_masked.hip"]
 ARCH = "gfx950"
 
 

@@ -211,6 +211,24 @@ HS_API hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, con
   return ok();
 }
 
+HS_API hs_status hs_compress_masked(const hs_shape *shape, const hs_counts *counts,
+                                    const uint16_t *k, const uint16_t *v, const uint8_t *mode_k,
+                                    const uint8_t *mode_v, const hs_cache *out,
+                                    int32_t *head_status, void *stream) {
+  hs::Dims d;
+  hs::CacheView c;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v"))) return st;
+  if ((st = check_ptr(mode_k, "mode_k")) || (st = check_ptr(mode_v, "mode_v"))) return st;
+  if ((st = check_ptr(head_status, "head_status", false))) return st;
+  if ((st = check_cache(out, d, &c))) return st;
+  hipError_t e = hs::launch_modes(d, mode_k, mode_v, c, head_status, (hipStream_t)stream);
+  if (e == hipSuccess) e = hs::launch_pack(d, k, v, c, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "masked compress launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 HS_API hs_status hs_recompress(const hs_shape *shape, const hs_counts *in_counts,
                                const hs_cache *in, const hs_counts *out_counts,
                                const hs_cache *out, void *ws, size_t ws_bytes, void *stream) {

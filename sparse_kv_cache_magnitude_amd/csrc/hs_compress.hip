@@ -340,6 +340,12 @@ hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, 
                                                    c.map_v);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_pack(d, k, v, c, stream);
+}
+
+hipError_t launch_pack(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
+                       hipStream_t stream) {
+  const dim3 grid(d.nb, d.b * d.hkv);
   if (d.B == 64)
     k_pack<64><<<grid, 256, 0, stream>>>(k, v, c.map_k, c.map_v, c, d.L);
   else

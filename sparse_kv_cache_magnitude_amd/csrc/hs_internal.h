@@ -24,6 +24,15 @@ struct CacheView {
 hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
                            uint64_t *keys, hipStream_t stream);
 
+// The pack step alone: pools written from K, V as c.map_k / c.map_v (already on the device) say.
+hipError_t launch_pack(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
+                       hipStream_t stream);
+
+// Caller-given block modes (uint8 [b][hkv][nb], 0 pruned / 1 dense / 2 2:4) -> index maps, with
+// per-head validation (hs_masked.hip). head_status may be null.
+hipError_t launch_modes(const Dims &d, const uint8_t *mode_k, const uint8_t *mode_v,
+                        const CacheView &c, int32_t *head_status, hipStream_t stream);
+
 // counters: one uint32 per (batch entry, KV head, column group of 16 query heads), zero before
 // the call and zero again after it.
 hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,

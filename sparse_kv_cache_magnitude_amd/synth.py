@@ -60,6 +60,42 @@ def make_q(seed: int, b: int, hq: int, lq: int, D: int):
     return bf16_bits(rq.standard_normal((b, hq, lq, D), dtype=np.float32))
 
 
+def random_modes(seed: int, b: int, hkv: int, nb: int, n_p: int, n_sk: int, n_sv: int):
+    """Caller-side block-level masks with exact per-head counts: uint8 [b][hkv][nb] for K and V
+    (0 pruned, 1 dense, 2 2:4), the pruned blocks shared, placed uniformly at random."""
+    rng = np.random.default_rng(seed)
+    mk = np.ones((b, hkv, nb), np.uint8)
+    mv = np.ones((b, hkv, nb), np.uint8)
+    for bi in range(b):
+        for h in range(hkv):
+            perm = rng.permutation(nb)
+            mk[bi, h, perm[:n_p]] = 0
+            mv[bi, h, perm[:n_p]] = 0
+            rest = perm[n_p:]
+            mk[bi, h, rng.permutation(rest)[:n_sk]] = 2
+            mv[bi, h, rng.permutation(rest)[:n_sv]] = 2
+    return mk, mv
+
+
+def random_element_mask(seed: int, X: np.ndarray, modes: np.ndarray, B: int, along_tokens: bool,
+                        keep: int = 2):
+    """X [b][hkv][L][D] bf16 bits with a random caller-side element mask applied in the blocks
+    whose mode is 2: in each group of four (consecutive channels of a token, or consecutive
+    tokens of a channel if along_tokens) all but `keep` random positions are set to +0."""
+    rng = np.random.default_rng(seed)
+    b, hkv, L, D = X.shape
+    out = X.copy()
+    for bi in range(b):
+        for h in range(hkv):
+            for i in np.flatnonzero(modes[bi, h] == 2):
+                blk = out[bi, h, i * B:(i + 1) * B]
+                g = blk.T.reshape(D, B // 4, 4) if along_tokens else blk.reshape(B, D // 4, 4)
+                r = rng.random(g.shape).argsort(axis=-1)      # a random order of the 4 positions
+                g[r >= keep] = 0
+                blk[...] = g.reshape(D, B).T if along_tokens else g.reshape(B, D)
+    return out
+
+
 def block_count(frac: float, nb: int) -> int:
     """Block fraction -> integer count, round half up."""
     return int(np.floor(frac * nb + 0.5))

@@ -177,6 +177,27 @@ def test_workspace_checks():
         == hs.HS_ERR_SHAPE
 
 
+def _masked(shp, cnt, k, v, mk, mv, cache, status):
+    _raise(hs.lib().hs_compress_masked(ctypes.byref(shp), ctypes.byref(cnt), k, v, mk, mv,
+                                       ctypes.byref(_cache_struct(cache)), status, None))
+
+
+def test_compress_masked_validation():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    call = lambda shp=SHP, cnt=CNT, k=FAKE, v=FAKE, mk=FAKE, mv=FAKE, c=cache, st=MISALIGNED: \
+        _status(lambda: _masked(shp, cnt, k, v, mk, mv, c, st))
+    # head_status is optional but, when given, must be aligned: every call below fails before
+    # a launch because one argument is invalid
+    assert call() == hs.HS_ERR_ALIGN
+    for name in ("k", "v", "mk", "mv"):
+        assert call(**{name: None}) == hs.HS_ERR_NULL, name
+        assert call(**{name: MISALIGNED}) == hs.HS_ERR_ALIGN, name
+    for f in hs.CACHE_FIELDS:
+        assert call(c=dict(cache, **{f: None}), st=None) == hs.HS_ERR_NULL
+    assert call(cnt=hs.counts(9, 8, 0), st=None) == hs.HS_ERR_COUNTS
+    assert call(shp=hs.shape(1, 4, 1, 1024, 128, 32), st=None) == hs.HS_ERR_SHAPE
+
+
 def _disjoint_caches():
     """Placeholder input and output caches whose arrays are far apart, and a workspace address."""
     cin = {f: (1 << 40) + (i << 32) for i, f in enumerate(hs.CACHE_FIELDS)}

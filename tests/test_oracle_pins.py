@@ -4,6 +4,7 @@ Each test checks the oracle against something other than itself: brute-force enu
 rational arithmetic, the paper's printed worked values (tests/golden), a library routine
 (torch scaled_dot_product_attention in float64), or an identity that holds exactly.
 """
+import itertools
 import json
 import math
 import os
@@ -222,6 +223,121 @@ def test_recompress_changes_modes_by_the_held_values():
     again = oracle.recompress(d_first, first, Dims(1, 1, d.L, d.D, d.B, 0, 4, 0))
     # the three 2:4 blocks keep their mode (zero loss) and one more is chosen among the rest
     assert ((first["map_k"] < 0) <= (again["map_k"] < 0)).all() and (again["map_k"] < 0).sum() == 4
+
+
+# ------------------------------------------------------------------------------------------------
+# Compression with caller masks ([HS] §III-A cache pruner, §IV-B generic kernel)
+
+def modes_of(d, cache):
+    """Block modes (0 pruned, 1 dense, 2 2:4) read off a compressed cache's maps."""
+    out = []
+    for m in (cache["map_k"], cache["map_v"]):
+        m = np.asarray(m).reshape(d.b, d.hkv, d.nb)
+        out.append(np.where(m == 0, 0, np.where(m > 0, 1, 2)).astype(np.uint8))
+    return out
+
+
+@pytest.mark.parametrize("maker", [tie_heavy, normal])
+@pytest.mark.parametrize("counts", [(0, 3, 5), (2, 3, 4), (3, 5, 0), (0, 8, 8), (8, 0, 0)])
+def test_masked_reproduces_the_magnitude_compressor(maker, counts):
+    d = Dims(2, 2, 256, 32, 32, *counts)
+    K = maker((d.b, d.hkv, d.L, d.D), 41)
+    V = maker((d.b, d.hkv, d.L, d.D), 42)
+    want = oracle.compress(d, K, V)
+    mk, mv = modes_of(d, want)
+    # fed the magnitude compressor's own block modes and its masked (unpacked) values, the
+    # generic path writes the same cache: the non-zeros of a thinned group are its top two
+    Kt, Vt, _ = oracle.unpack(d, want)
+    got = oracle.compress_masked(d, Kt, Vt, mk, mv)
+    assert not got["head_status"].any()
+    _same_cache(got, want)
+    # unmasked input: groups with more than two non-zeros fall back to the top-2 rule
+    _same_cache(oracle.compress_masked(d, K, V, mk, mv), want)
+
+
+def test_masked_element_rule_brute_force():
+    """Every group over {+0, -0, 1, -2} (256 of them), stored by the generic kernel's rule: the
+    non-zeros padded with the lowest zero positions, or the top-2 pair when more than two."""
+    vals = np.array([0x0000, 0x8000, 0x3F80, 0xC000], np.uint16)
+    groups = np.array(list(itertools.product(range(4), repeat=4)))
+    X4 = vals[groups]                                              # [256][4]
+    blockK = X4.reshape(64, 16)                                    # 64 tokens x 4 groups
+    K = np.zeros((1, 1, 64, 16), np.uint16)
+    K[0, 0] = blockK
+    V = np.zeros((1, 1, 64, 16), np.uint16)
+    V[0, 0] = X4.reshape(16, 64).T            # channel c, token group g holds group 16 c + g
+    d = Dims(1, 1, 64, 16, 64, 0, 1, 1)
+    two = np.full((1, 1, 1), 2, np.uint8)
+    got = oracle.compress_masked(d, K, V, two, two)
+    _, _, _, keepK, keepV = pinlib.decode_cache(1, 1, 64, 16, 64, got)
+
+    def expected(x4):
+        nz = [j for j in range(4) if x4[j] & 0x7FFF]
+        if len(nz) > 2:
+            return set(pinlib.kept_pair_brute(x4))
+        return set(nz) | set([j for j in range(4) if not x4[j] & 0x7FFF][:2 - len(nz)])
+
+    kk = keepK[0, 0].reshape(64, 4, 4)
+    vv = keepV[0, 0].T.reshape(16, 16, 4)
+    for n, x4 in enumerate(X4):
+        want = expected(x4)
+        assert set(np.flatnonzero(kk[n // 4, n % 4])) == want, x4
+    Vg = V[0, 0].T.reshape(16, 16, 4)
+    for c in range(16):
+        for g in range(16):
+            assert set(np.flatnonzero(vv[c, g])) == expected(Vg[c, g]), Vg[c, g]
+
+
+def test_masked_channel_mask_closed_form():
+    """A channel mask (K keeps channels 4g, 4g+1 of every group; V keeps tokens 4g, 4g+2): every
+    K metadata word is 0x4444 (positions 0 and 1 in each nibble), every V word 0x8888 (0, 2),
+    and the kept values are the unmasked ones in order."""
+    d = Dims(1, 2, 128, 32, 32, 0, 4, 4)
+    K = normal((1, 2, 128, 32), 51)
+    V = normal((1, 2, 128, 32), 52)
+    K[..., 2::4] = 0
+    K[..., 3::4] = 0
+    V[:, :, 1::4] = 0
+    V[:, :, 3::4] = 0
+    two = np.full((1, 2, 4), 2, np.uint8)
+    got = oracle.compress_masked(d, K, V, two, two)
+    assert (got["k_meta"] == 0x4444).all() and (got["v_meta"] == 0x8888).all()
+    kn = got["k_nnz"].reshape(2, 4, 32, 8, 2)                      # [head][block][token][group][2]
+    want_k = K[0].reshape(2, 4, 32, 8, 4)[..., :2]
+    assert (kn == want_k).all()
+    vn = got["v_nnz"].reshape(2, 4, 32, 8, 2)                      # [head][block][chan][group][2]
+    want_v = V[0].reshape(2, 4, 32, 32).transpose(0, 1, 3, 2).reshape(2, 4, 32, 8, 4)[..., [0, 2]]
+    assert (vn == want_v).all()
+
+
+def test_masked_rejects_heads_whose_modes_do_not_fit():
+    d = Dims(2, 3, 256, 32, 32, 2, 3, 4)
+    K = normal((2, 3, 256, 32), 61)
+    V = normal((2, 3, 256, 32), 62)
+    mk, mv = synth.random_modes(63, 2, 3, 8, 2, 3, 4)
+    good = oracle.compress_masked(d, K, V, mk, mv)
+    assert not good["head_status"].any()
+    bk, bv = mk.copy(), mv.copy()
+    bk[0, 1, np.flatnonzero(bk[0, 1] == 1)[0]] = 3                 # a byte above 2 (counts of 0
+                                                                   # and 2 unchanged)
+    i = np.flatnonzero(bk[1, 0] == 0)[0]
+    bk[1, 0, i] = 1                                                # K kept where V pruned: 2 | 4
+    j = np.flatnonzero(bv[1, 2] == 1)[0]
+    bv[1, 2, j] = 2                                                # one 2:4 V block too many
+    got = oracle.compress_masked(d, K, V, bk, bv)
+    st = got["head_status"]
+    assert st[0, 1] == 1 and st[1, 0] == 2 | 4 and st[1, 2] == 4
+    assert st[0, 0] == st[0, 2] == st[1, 1] == 0
+    for m in ("map_k", "map_v"):
+        gm, wm = got[m].reshape(2, 3, 8), good[m].reshape(2, 3, 8)
+        ok = st == 0
+        assert (gm[~ok] == 0).all() and (gm[ok] == wm[ok]).all()
+    # accepted heads' pool slots are written exactly as before; rejected ones are left zero
+    Kt, Vt, _, _, _ = pinlib.decode_cache(2, 3, 256, 32, 32, got)
+    Kg, Vg, _, _, _ = pinlib.decode_cache(2, 3, 256, 32, 32, good)
+    ok = (st == 0)[..., None, None]
+    assert (np.where(ok, Kt, 0) == np.where(ok, Kg, 0)).all()
+    assert (np.where(ok, Vt, 0) == np.where(ok, Vg, 0)).all()
 
 
 def test_rejects_out_of_range_inputs():
