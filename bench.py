@@ -31,7 +31,7 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
-SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked")
+SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked", "policy")
 COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
 COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
 
@@ -61,8 +61,8 @@ def parse():
                    help="instead of the headline step: one JSON line per further workload; PARTS "
                         "is a comma list of " + ", ".join(SUITE_PARTS) + " (default: all): 16K "
                         "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, the "
-                        "prefill-to-decode re-compression and the caller-mask compressor at 32K "
-                        "batch 8")
+                        "prefill-to-decode re-compression, the caller-mask compressor and the "
+                        "sink/local dense policy at 32K batch 8")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -307,6 +307,8 @@ def run_suite(parts=SUITE_PARTS, reps=7):
         suite_recompress(hs, synth, setup, timed, emit, torch)
     if "masked" in parts:
         suite_masked(hs, synth, setup, timed, emit, torch)
+    if "policy" in parts:
+        suite_policy(hs, synth, setup, timed, decode_time, emit)
     return 0
 
 
@@ -443,6 +445,27 @@ def suite_masked(hs, synth, setup, timed, emit, torch):
           "magnitude_compress_us": round(comp * 1e6, 1), "bytes": nbytes,
           "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
     del K, V, Km, Vm, cache
+
+def suite_policy(hs, synth, setup, timed, decode_time, emit):
+    """The 32K batch-8 cache compressed with the quality runs' dense policy (first 64 and last 256
+    tokens dense, unranked) at the workload's counts, against the plain compressor, and the decode
+    on both caches."""
+    w = synth.workload("decode_llama8b_32k_b8")
+    G = w.hq // w.hkv
+    K, V, Q, q, shp, cnt, cache, comp = setup(w)
+    del Q
+    pol = hs.policy(64, 256)
+    cache_p = hs.alloc_cache(shp, cnt)
+    ws = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+    t_c = timed(lambda: hs.hs_compress_ex(shp, cnt, pol, K, V, cache_p, ws))
+    t = decode_time(shp, cnt, cache, q)
+    t_p = decode_time(shp, cnt, cache_p, q)
+    nbytes = decode_bytes(w, G)
+    emit({"suite": w.name + "_policy_sink64_local256", "compress_policy_us": round(t_c * 1e6, 1),
+          "compress_us": round(comp * 1e6, 1), "decode_policy_us": round(t_p * 1e6, 2),
+          "decode_us": round(t * 1e6, 2), "decode_bytes": nbytes,
+          "decode_policy_gbs": round(nbytes / t_p / 1e9, 1)})
+    del K, V, q, cache, cache_p
 
 def main():
     args = parse()

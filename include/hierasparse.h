@@ -14,6 +14,8 @@
  *                    K dense and V 2:4 for prefill, then both 2:4 for decode).
  *   hs_compress_masked  [HS] §III-A cache pruner fed by any pruning algorithm's block-level and
  *                    element-level masks + §IV-B generic compression kernel.
+ *   hs_compress_ex   hs_compress with the sink / local-window dense policy of the quality runs
+ *                    ([HS] §V-A).
  *
  * Conventions shared by every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
@@ -103,6 +105,12 @@ typedef struct {
   size_t map_k, map_v, k_dense, k_nnz, k_meta, v_dense, v_nnz, v_meta;
 } hs_cache_bytes;
 
+/* Tokens kept dense by hs_compress_ex: the first sink_tokens and the last local_tokens of the
+   sequence ([HS] §V-A keeps 64 and 256). */
+typedef struct {
+  int32_t sink_tokens, local_tokens;
+} hs_policy;
+
 enum { HS_OP_COMPRESS = 1, HS_OP_DECODE = 2, HS_OP_RECOMPRESS = 3 };
 
 /* Prefill flags: how 2:4 blocks reach the matrix cores. */
@@ -130,6 +138,16 @@ hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *coun
 hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
                       const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
                       void *stream);
+
+/* hs_compress with a dense policy: every block holding one of the first policy->sink_tokens or
+   the last policy->local_tokens tokens is dense for K and V and takes no part in the ranking;
+   the counts select among the other blocks, so n_pruned + n_sparse_k and n_pruned + n_sparse_v
+   must not exceed their number (HS_ERR_COUNTS, also for a negative token count or one above
+   seq_len). policy = NULL or {0, 0} is hs_compress. Same workspace as hs_compress
+   (HS_OP_COMPRESS). Deterministic. */
+hs_status hs_compress_ex(const hs_shape *shape, const hs_counts *counts, const hs_policy *policy,
+                         const uint16_t *k, const uint16_t *v, const hs_cache *out, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* Compress with the caller's masks instead of the magnitude ranking. mode_k, mode_v: uint8
    [batch][kv_heads][nb] device arrays, one per block: 0 = pruned, 1 = dense, 2 = 2:4. The element

@@ -6,7 +6,8 @@ this package; the GPU library and its Python binding never import it.
 What each function follows is cited in hso.c ("HieraSparse", arXiv 2604.16864v2: Eq. (1),
 Eq. (2a)-(2d), §III-B, §IV-A/B) together with the readings R1-R8 taken where the paper is silent;
 recompress (§III, Fig. 3) is the composition of unpack and compress (R9), compress_masked the
-generic compressor fed by caller masks (§III-A, §IV-B; R10).
+generic compressor fed by caller masks (§III-A, §IV-B; R10), and compress(sink=, local=) the
+dense policy of the quality runs (§V-A; R11).
 Parity is pinned by the tests under tests/ (brute force, closed forms, library routines, identities).
 """
 import ctypes
@@ -36,12 +37,13 @@ def _lib():
         P = ctypes.c_void_p
         lib.hso_pool_elems.argtypes = [ctypes.POINTER(_Dims), P]
         lib.hso_compress.argtypes = [ctypes.POINTER(_Dims)] + [P] * 12
+        lib.hso_compress_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int, ctypes.c_int] + [P] * 12
         lib.hso_unpack.argtypes = [ctypes.POINTER(_Dims)] + [P] * 11
         lib.hso_compress_masked.argtypes = [ctypes.POINTER(_Dims)] + [P] * 13
         lib.hso_attention.argtypes = [ctypes.c_int] * 8 + [P] * 4 + [ctypes.c_double,
                                                                       ctypes.c_int64, P, P, P]
         for f in (lib.hso_pool_elems, lib.hso_compress, lib.hso_unpack, lib.hso_attention,
-                  lib.hso_compress_masked):
+                  lib.hso_compress_masked, lib.hso_compress_ex):
             f.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -90,10 +92,12 @@ def pool_bytes(d: Dims) -> dict:
     return {k: v * (4 if k.startswith("map") else 2) for k, v in pool_elems(d).items()}
 
 
-def compress(d: Dims, K: np.ndarray, V: np.ndarray, with_loss: bool = False) -> dict:
+def compress(d: Dims, K: np.ndarray, V: np.ndarray, with_loss: bool = False, sink: int = 0,
+             local: int = 0) -> dict:
     """Compress bf16-bit tensors K, V [b][Hkv][L][D] (uint16). Returns the maps, the six pools
     (flat arrays) and 'keys' [b][Hkv][nb][3] uint64 (K 2:4 loss, V 2:4 loss, whole-block loss);
-    with_loss adds the same losses in fp64 as 'loss'."""
+    with_loss adds the same losses in fp64 as 'loss'. sink / local: the dense policy of hso.c
+    R11 (blocks holding one of the first sink or last local tokens stay dense, unranked)."""
     K = np.ascontiguousarray(K, dtype=np.uint16)
     V = np.ascontiguousarray(V, dtype=np.uint16)
     assert K.shape == V.shape == (d.b, d.hkv, d.L, d.D)
@@ -101,8 +105,8 @@ def compress(d: Dims, K: np.ndarray, V: np.ndarray, with_loss: bool = False) -> 
     out = {k: np.zeros(n[k], np.int32 if k.startswith("map") else np.uint16) for k in POOLS}
     keys = np.zeros((d.b, d.hkv, d.nb, 3), np.uint64)
     loss = np.zeros((d.b, d.hkv, d.nb, 3), np.float64) if with_loss else None
-    _check(_lib().hso_compress(ctypes.byref(d.c()), _ptr(K), _ptr(V),
-                               *[_ptr(out[k]) for k in POOLS], _ptr(keys), _ptr(loss)))
+    _check(_lib().hso_compress_ex(ctypes.byref(d.c()), int(sink), int(local), _ptr(K), _ptr(V),
+                                  *[_ptr(out[k]) for k in POOLS], _ptr(keys), _ptr(loss)))
     out["keys"] = keys
     if with_loss:
         out["loss"] = loss

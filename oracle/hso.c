@@ -43,6 +43,9 @@
  *      with more than two non-zeros violates the mask and falls back to R1's top-2. A (batch,
  *      KV head) whose block modes do not match the pool counts is rejected: all-pruned map, no
  *      pool writes, a status bit.
+ *   R11 dense policy ([HS] §V-A quality runs): a block holding any of the first 'sink' or the last
+ *      'local' tokens stays dense for K and V and is not ranked; the counts select among the
+ *      others.
  */
 #include <math.h>
 #include <stdint.h>
@@ -220,21 +223,24 @@ static void block_keys(const hso_dims *d, const uint16_t *Kh, const uint16_t *Vh
   }
 }
 
-/* Block modes of one head: mode_k[i], mode_v[i] in {0 = pruned, 1 = dense, 2 = 2:4}. */
-static void block_modes(const hso_dims *d, const uint64_t *keys, int *mode_k, int *mode_v,
-                        ranked *scratch) {
-  int nb = d->L / d->B;
+/* Block modes of one head: mode_k[i], mode_v[i] in {0 = pruned, 1 = dense, 2 = 2:4}. Blocks with
+   held[i] set stay dense and are not ranked (R11). */
+static void block_modes(const hso_dims *d, const uint64_t *keys, const char *held, int *mode_k,
+                        int *mode_v, ranked *scratch) {
+  int nb = d->L / d->B, n = 0;
   /* R3 step 1: the n_p blocks with the smallest whole-block loss are pruned. */
-  for (int i = 0; i < nb; ++i) { scratch[i].key = keys[3 * i + 2]; scratch[i].idx = i; }
-  qsort(scratch, nb, sizeof(ranked), ranked_cmp);
+  for (int i = 0; i < nb; ++i)
+    if (!held[i]) { scratch[n].key = keys[3 * i + 2]; scratch[n].idx = i; ++n; }
+  qsort(scratch, n, sizeof(ranked), ranked_cmp);
   for (int i = 0; i < nb; ++i) { mode_k[i] = 1; mode_v[i] = 1; }
   for (int r = 0; r < d->n_p; ++r) { mode_k[scratch[r].idx] = 0; mode_v[scratch[r].idx] = 0; }
   /* Eq. (2d) per tensor among the survivors: the n_sX smallest 2:4 losses become 2:4. */
   for (int t = 0; t < 2; ++t) {
     int *mode = t ? mode_v : mode_k;
-    int want = t ? d->n_sv : d->n_sk, n = 0;
+    int want = t ? d->n_sv : d->n_sk;
+    n = 0;
     for (int i = 0; i < nb; ++i)
-      if (mode[i] != 0) { scratch[n].key = keys[3 * i + t]; scratch[n].idx = i; ++n; }
+      if (!held[i] && mode[i] != 0) { scratch[n].key = keys[3 * i + t]; scratch[n].idx = i; ++n; }
     qsort(scratch, n, sizeof(ranked), ranked_cmp);
     for (int r = 0; r < want; ++r) mode[scratch[r].idx] = 2;
   }
@@ -310,15 +316,33 @@ static void write_head(const hso_dims *d, int64_t hd, const uint16_t *Kh, const 
  * by hso_pool_elems. keys (optional, [b][hkv][nb][3] uint64) and loss (optional, same shape,
  * fp64) receive the block losses. Returns HSO_ERR_VALUE if an input is non-finite or |x| >= 2^24.
  */
-int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_t *map_k,
-                 int32_t *map_v, uint16_t *k_dense, uint16_t *k_nnz, uint16_t *k_meta,
-                 uint16_t *v_dense, uint16_t *v_nnz, uint16_t *v_meta, uint64_t *keys_out,
-                 double *loss_out) {
+int hso_compress_ex(const hso_dims *d, int sink, int local, const uint16_t *K, const uint16_t *V,
+                    int32_t *map_k, int32_t *map_v, uint16_t *k_dense, uint16_t *k_nnz,
+                    uint16_t *k_meta, uint16_t *v_dense, uint16_t *v_nnz, uint16_t *v_meta,
+                    uint64_t *keys_out, double *loss_out) {
   int rc = dims_check(d);
   if (rc) return rc;
+  /* R11: a block holding any of the first 'sink' or the last 'local' tokens is not ranked. */
+  if (sink < 0 || local < 0 || sink > d->L || local > d->L) return HSO_ERR_COUNTS;
+  const int nblk = d->L / d->B;
+  char *held = (char *)malloc(nblk);
+  int n_ranked = 0;
+  for (int i = 0; i < nblk; ++i) {
+    held[i] = 0;
+    for (int t = i * d->B; t < (i + 1) * d->B; ++t)
+      if (t < sink || t >= d->L - local) held[i] = 1;
+    n_ranked += !held[i];
+  }
+  if (d->n_p + d->n_sk > n_ranked || d->n_p + d->n_sv > n_ranked) {
+    free(held);
+    return HSO_ERR_COUNTS;
+  }
   const int64_t heads = (int64_t)d->b * d->hkv, per_head = (int64_t)d->L * d->D;
   for (int64_t e = 0; e < heads * per_head; ++e)
-    if (!bf16_in_range(K[e]) || !bf16_in_range(V[e])) return HSO_ERR_VALUE;
+    if (!bf16_in_range(K[e]) || !bf16_in_range(V[e])) {
+      free(held);
+      return HSO_ERR_VALUE;
+    }
 
   const int nb = d->L / d->B;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -330,7 +354,7 @@ int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_
     ranked *scratch = (ranked *)malloc(sizeof(ranked) * nb);
     block_keys(d, Kh, Vh, keys, loss);
     if (keys_out) memcpy(keys_out + hd * 3 * nb, keys, sizeof(uint64_t) * 3 * nb);
-    block_modes(d, keys, mode_k, mode_v, scratch);
+    block_modes(d, keys, held, mode_k, mode_v, scratch);
     write_head(d, hd, Kh, Vh, mode_k, mode_v, keep_two, map_k, map_v, k_dense, k_nnz, k_meta,
                v_dense, v_nnz, v_meta);
     free(keys);
@@ -338,7 +362,16 @@ int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_
     free(mode_v);
     free(scratch);
   }
+  free(held);
   return HSO_OK;
+}
+
+int hso_compress(const hso_dims *d, const uint16_t *K, const uint16_t *V, int32_t *map_k,
+                 int32_t *map_v, uint16_t *k_dense, uint16_t *k_nnz, uint16_t *k_meta,
+                 uint16_t *v_dense, uint16_t *v_nnz, uint16_t *v_meta, uint64_t *keys_out,
+                 double *loss_out) {
+  return hso_compress_ex(d, 0, 0, K, V, map_k, map_v, k_dense, k_nnz, k_meta, v_dense, v_nnz,
+                         v_meta, keys_out, loss_out);
 }
 
 /*

@@ -193,22 +193,45 @@ HS_API hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_count
   return ok();
 }
 
-HS_API hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
-                             const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
-                             void *stream) {
+HS_API hs_status hs_compress_ex(const hs_shape *shape, const hs_counts *counts,
+                                const hs_policy *policy, const uint16_t *k, const uint16_t *v,
+                                const hs_cache *out, void *ws, size_t ws_bytes, void *stream) {
   hs::Dims d;
   hs::CacheView c;
   hs_status st = make_dims(shape, counts, &d);
   if (st) return st;
+  // Blocks [dense_lo, dense_hi) are ranked; the others hold sink or local-window tokens.
+  int dense_lo = 0, dense_hi = d.nb;
+  if (policy) {
+    const int sink = policy->sink_tokens, local = policy->local_tokens;
+    if (sink < 0 || local < 0 || sink > d.L || local > d.L)
+      return fail(HS_ERR_COUNTS, "sink_tokens (%d) and local_tokens (%d) must be in 0..seq_len",
+                  sink, local);
+    dense_lo = (sink + d.B - 1) / d.B;
+    dense_hi = (d.L - local) / d.B;
+    const int ranked = dense_hi > dense_lo ? dense_hi - dense_lo : 0;
+    if (d.np + d.nsk > ranked || d.np + d.nsv > ranked)
+      return fail(HS_ERR_COUNTS,
+                  "n_pruned + n_sparse_{k,v} exceeds the %d blocks outside the dense policy",
+                  ranked);
+    if (ranked == 0) dense_hi = dense_lo;
+  }
   if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v"))) return st;
   if ((st = check_cache(out, d, &c))) return st;
   if (!ws || ws_bytes < compress_ws_bytes(d))
     return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", compress_ws_bytes(d),
                 ws_bytes, ws ? "" : ", NULL");
   if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
-  hipError_t e = hs::launch_compress(d, k, v, c, (uint64_t *)ws, (hipStream_t)stream);
+  hipError_t e = hs::launch_compress(d, k, v, c, (uint64_t *)ws, (hipStream_t)stream, dense_lo,
+                                     dense_hi);
   if (e != hipSuccess) return fail(HS_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+HS_API hs_status hs_compress(const hs_shape *shape, const hs_counts *counts, const uint16_t *k,
+                             const uint16_t *v, const hs_cache *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  return hs_compress_ex(shape, counts, nullptr, k, v, out, ws, ws_bytes, stream);
 }
 
 HS_API hs_status hs_compress_masked(const hs_shape *shape, const hs_counts *counts,

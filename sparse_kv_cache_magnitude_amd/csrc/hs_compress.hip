@@ -156,9 +156,11 @@ __device__ void bitonic_sort(uint64_t *key, uint16_t *idx, int n) {
   }
 }
 
+// Blocks i < dense_lo or i >= dense_hi are kept dense for K and V and take no part in the
+// ranking (the sink and local-window tokens); the counts apply to the blocks in between.
 __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restrict__ keys, int nb,
-                                                       int n_p, int n_sk, int n_sv,
-                                                       int32_t *__restrict__ map_k,
+                                                       int n_p, int n_sk, int n_sv, int dense_lo,
+                                                       int dense_hi, int32_t *__restrict__ map_k,
                                                        int32_t *__restrict__ map_v) {
   __shared__ uint64_t skey[kMaxBlocks];
   __shared__ uint16_t sidx[kMaxBlocks];
@@ -169,9 +171,11 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restric
   int n = 2;
   while (n < nb) n <<= 1;
 
-  // Pruned blocks: the n_p smallest whole-block magnitudes.
+  // Pruned blocks: the n_p smallest whole-block magnitudes among the blocks that may be pruned
+  // (a kept-dense block carries the largest key, which no real loss reaches).
+  auto ranked = [&](int t) { return t < nb && t >= dense_lo && t < dense_hi; };
   for (int t = tid; t < n; t += kRankThreads) {
-    skey[t] = t < nb ? hk[3 * t + 2] : ~0ull;
+    skey[t] = ranked(t) ? hk[3 * t + 2] : ~0ull;
     sidx[t] = (uint16_t)t;
   }
   __syncthreads();
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restric
   for (int x = 0; x < 2; ++x) {
     const int want = x ? n_sv : n_sk;
     for (int t = tid; t < n; t += kRankThreads) {
-      skey[t] = (t < nb && mode[x][t] != 0) ? hk[3 * t + x] : ~0ull;
+      skey[t] = (ranked(t) && mode[x][t] != 0) ? hk[3 * t + x] : ~0ull;
       sidx[t] = (uint16_t)t;
     }
     __syncthreads();
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ K,
 }  // namespace
 
 hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
-                           uint64_t *keys, hipStream_t stream) {
+                           uint64_t *keys, hipStream_t stream, int dense_lo, int dense_hi) {
   const dim3 grid(d.nb, d.b * d.hkv);
   if (d.B == 64)
     k_score<64><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
@@ -336,7 +340,8 @@ hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, 
     k_score<128><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_rank<<<d.b * d.hkv, kRankThreads, 0, stream>>>(keys, d.nb, d.np, d.nsk, d.nsv, c.map_k,
+  k_rank<<<d.b * d.hkv, kRankThreads, 0, stream>>>(keys, d.nb, d.np, d.nsk, d.nsv, dense_lo,
+                                                   dense_hi < 0 ? d.nb : dense_hi, c.map_k,
                                                    c.map_v);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

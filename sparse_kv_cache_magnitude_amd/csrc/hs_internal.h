@@ -21,8 +21,10 @@ struct CacheView {
   uint16_t *v_dense, *v_nnz, *v_meta;
 };
 
+// Blocks i < dense_lo or i >= dense_hi (dense_hi < 0: nb) stay dense and are not ranked.
 hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
-                           uint64_t *keys, hipStream_t stream);
+                           uint64_t *keys, hipStream_t stream, int dense_lo = 0,
+                           int dense_hi = -1);
 
 // The pack step alone: pools written from K, V as c.map_k / c.map_v (already on the device) say.
 hipError_t launch_pack(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,

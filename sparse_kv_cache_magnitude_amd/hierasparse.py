@@ -17,8 +17,9 @@ HS_ERR_WORKSPACE, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_OVERLAP = 5, 6, 7, 8
 HS_OP_COMPRESS, HS_OP_DECODE, HS_OP_RECOMPRESS = 1, 2, 3
 HS_PREFILL_SMFMAC, HS_PREFILL_DECOMPRESS = 0, 1
 
-EXPORTS = ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_masked",
-           "hs_recompress", "hs_decode_attn", "hs_prefill_attn", "hs_status_string", "hs_last_error")
+EXPORTS = ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
+           "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_prefill_attn",
+           "hs_status_string", "hs_last_error")
 
 CACHE_FIELDS = ("map_k", "map_v", "k_dense", "k_nnz", "k_meta", "v_dense", "v_nnz", "v_meta")
 
@@ -38,6 +39,10 @@ class HsCache(ctypes.Structure):
 
 class HsCacheBytes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in CACHE_FIELDS]
+
+
+class HsPolicy(ctypes.Structure):
+    _fields_ = [("sink_tokens", ctypes.c_int32), ("local_tokens", ctypes.c_int32)]
 
 
 class HsError(RuntimeError):
@@ -61,6 +66,8 @@ def lib():
         L.hs_workspace_size.argtypes = [ctypes.c_int, S(HsShape), S(HsCounts), ctypes.c_int32,
                                         S(ctypes.c_size_t)]
         L.hs_compress.argtypes = [S(HsShape), S(HsCounts), P, P, S(HsCache), P, ctypes.c_size_t, P]
+        L.hs_compress_ex.argtypes = [S(HsShape), S(HsCounts), S(HsPolicy), P, P, S(HsCache), P,
+                                     ctypes.c_size_t, P]
         L.hs_compress_masked.argtypes = [S(HsShape), S(HsCounts), P, P, P, P, S(HsCache), P, P]
         L.hs_recompress.argtypes = [S(HsShape), S(HsCounts), S(HsCache), S(HsCounts), S(HsCache),
                                     P, ctypes.c_size_t, P]
@@ -68,8 +75,8 @@ def lib():
                                      ctypes.c_int32, P, ctypes.c_size_t, P]
         L.hs_prefill_attn.argtypes = [S(HsShape), S(HsCounts), S(HsCache), P, P, P,
                                       ctypes.c_float, ctypes.c_uint32, P]
-        for f in ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_masked",
-                  "hs_recompress", "hs_decode_attn", "hs_prefill_attn"):
+        for f in ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
+                  "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_prefill_attn"):
             getattr(L, f).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -136,6 +143,18 @@ def hs_compress(shp, cnt, k, v, cache, ws, stream=None):
                              ctypes.byref(_cache_struct(cache)), _ptr(ws),
                              ws.numel() * ws.element_size() if ws is not None else 0,
                              _stream(stream)))
+
+
+def policy(sink_tokens=64, local_tokens=256):
+    return HsPolicy(sink_tokens, local_tokens)
+
+
+def hs_compress_ex(shp, cnt, pol, k, v, cache, ws, stream=None):
+    _check(lib().hs_compress_ex(ctypes.byref(shp), ctypes.byref(cnt),
+                                ctypes.byref(pol) if pol is not None else None, _ptr(k), _ptr(v),
+                                ctypes.byref(_cache_struct(cache)), _ptr(ws),
+                                ws.numel() * ws.element_size() if ws is not None else 0,
+                                _stream(stream)))
 
 
 def hs_compress_masked(shp, cnt, k, v, mode_k, mode_v, cache, head_status=None, stream=None):

@@ -78,11 +78,12 @@ def lowest_set(keys, candidates, n):
     return set(best)
 
 
-def modes_brute(keys, n_p, n_sk, n_sv):
-    """Block modes (0 pruned, 1 dense, 2 2:4) of one head from its exact keys, by enumeration."""
+def modes_brute(keys, n_p, n_sk, n_sv, held=()):
+    """Block modes (0 pruned, 1 dense, 2 2:4) of one head from its exact keys, by enumeration;
+    blocks in `held` stay dense and are no candidates."""
     nb = len(keys)
-    pruned = lowest_set([k[2] for k in keys], range(nb), n_p)
-    surv = [i for i in range(nb) if i not in pruned]
+    pruned = lowest_set([k[2] for k in keys], [i for i in range(nb) if i not in held], n_p)
+    surv = [i for i in range(nb) if i not in pruned and i not in held]
     sk = lowest_set([k[0] for k in keys], surv, n_sk)
     sv = lowest_set([k[1] for k in keys], surv, n_sv)
     mk = [0 if i in pruned else (2 if i in sk else 1) for i in range(nb)]

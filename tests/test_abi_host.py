@@ -177,6 +177,31 @@ def test_workspace_checks():
         == hs.HS_ERR_SHAPE
 
 
+def _compress_ex(shp, cnt, pol, k, v, cache, ws, ws_bytes):
+    _raise(hs.lib().hs_compress_ex(ctypes.byref(shp), ctypes.byref(cnt),
+                                   ctypes.byref(pol) if pol is not None else None, k, v,
+                                   ctypes.byref(_cache_struct(cache)), ws, ws_bytes, None))
+
+
+def test_compress_ex_policy_validation():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    shp = hs.shape(1, 4, 1, 1024, 128, 64)                       # 16 blocks
+    need = hs.hs_workspace_size(hs.HS_OP_COMPRESS, shp, hs.counts(2, 4, 5))
+    call = lambda cnt, pol, n=need, k=FAKE: \
+        _status(lambda: _compress_ex(shp, cnt, pol, k, FAKE, cache, FAKE, n))
+    # sink 64 + local 256 hold 1 + 4 blocks: 11 are ranked
+    assert call(hs.counts(2, 10, 0), hs.policy(64, 256)) == hs.HS_ERR_COUNTS
+    assert call(hs.counts(2, 0, 10), hs.policy(64, 256)) == hs.HS_ERR_COUNTS
+    assert call(hs.counts(1, 10, 0), hs.policy(65, 256)) == hs.HS_ERR_COUNTS   # sink spills over
+    assert call(hs.counts(0, 0, 0), hs.policy(-1, 0)) == hs.HS_ERR_COUNTS
+    assert call(hs.counts(0, 0, 0), hs.policy(0, 1025)) == hs.HS_ERR_COUNTS
+    # counts that fit pass the policy check and fail on the next invalid argument
+    assert call(hs.counts(1, 10, 10), hs.policy(64, 256), k=None) == hs.HS_ERR_NULL
+    assert call(hs.counts(0, 0, 0), hs.policy(1024, 1024), k=None) == hs.HS_ERR_NULL
+    assert call(hs.counts(2, 4, 5), hs.policy(64, 256), n=need - 8) == hs.HS_ERR_WORKSPACE
+    assert call(hs.counts(2, 4, 5), None, n=need - 8) == hs.HS_ERR_WORKSPACE
+
+
 def _masked(shp, cnt, k, v, mk, mv, cache, status):
     _raise(hs.lib().hs_compress_masked(ctypes.byref(shp), ctypes.byref(cnt), k, v, mk, mv,
                                        ctypes.byref(_cache_struct(cache)), status, None))

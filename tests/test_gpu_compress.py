@@ -106,3 +106,37 @@ def test_compress_keys_bit_exact(B):
     want = oracle.compress(Dims(b, hkv, L, 128, B, *counts), K, V)
     assert np.array_equal(got, want["keys"]), np.argwhere(got != want["keys"])[:8]
     gu.compare_cache(gu.cache_to_numpy(cache), want)
+
+
+def _check_policy(b, hkv, L, B, counts, sink, local, K, V, hq=None):
+    hq = hq or hkv
+    shp, cnt = hs.shape(b, hq, hkv, L, 128, B), hs.counts(*counts)
+    print(f"[compress_ex] b={b} hkv={hkv} L={L} B={B} counts={counts} sink={sink} "
+          f"local={local}", flush=True)
+    cache = hs.alloc_cache(shp, cnt)
+    ws = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+    hs.hs_compress_ex(shp, cnt, hs.policy(sink, local), gu.to_dev(K), gu.to_dev(V), cache, ws)
+    torch.cuda.synchronize()
+    want = oracle.compress(Dims(b, hkv, L, 128, B, *counts), K, V, sink=sink, local=local)
+    gu.compare_cache(gu.cache_to_numpy(cache), want)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("sink,local", [(0, 0), (64, 256), (1, 1), (65, 0), (0, 129),
+                                        (300, 500)])
+def test_compress_dense_policy(B, sink, local):
+    rng = np.random.default_rng(B + sink + local)
+    b, hkv, L = 2, 2, 16 * B
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    held = len({i for i in range(16) for t in (i * B, i * B + B - 1)
+                if i * B < sink or i * B + B - 1 >= L - local})
+    r = 16 - held
+    _check_policy(b, hkv, L, B, (r // 4, r - r // 4, r // 2), sink, local, K, V)
+
+
+def test_compress_dense_policy_workload():
+    """The 32K batch-8 cache with the quality runs' policy (64 sink, 256 local-window tokens)."""
+    w = synth.workload("decode_llama8b_32k_b8")
+    K, V = gu.workload_kv(w.name)
+    _check_policy(w.b, w.hkv, w.L, w.B, w.counts(), 64, 256, K, V, hq=w.hq)

@@ -176,6 +176,48 @@ def test_round_trip_and_map_is_a_bijection():
 
 
 # ------------------------------------------------------------------------------------------------
+# Dense policy of the quality runs ([HS] §V-A): sink and local-window blocks stay dense
+
+@pytest.mark.parametrize("sink,local", [(0, 0), (1, 0), (16, 0), (17, 40), (0, 16), (0, 33),
+                                        (48, 48)])
+def test_dense_policy_brute_force(sink, local):
+    # a block is held when any of its tokens is a sink or local-window token
+    held = {i for i in range(8)
+            if any(t < sink or t >= 128 - local for t in range(16 * i, 16 * i + 16))}
+    r = 8 - len(held)
+    n_p = r // 3
+    n_sk, n_sv = r - n_p - (r > 3), min(r - n_p, 3)
+    d = Dims(b=1, hkv=2, L=128, D=16, B=16, n_p=n_p, n_sk=n_sk, n_sv=n_sv)
+    K = tie_heavy((1, 2, 128, 16), 71)
+    V = tie_heavy((1, 2, 128, 16), 72)
+    got = oracle.compress(d, K, V, sink=sink, local=local)
+    mk = got["map_k"].reshape(2, 8)
+    mv = got["map_v"].reshape(2, 8)
+    for h in range(2):
+        keys = pinlib.block_keys_exact(K[0, h], V[0, h], 16, 16)
+        want_k, want_v = pinlib.modes_brute(keys, n_p, n_sk, n_sv, held)
+        got_k = [0 if m == 0 else (1 if m > 0 else 2) for m in mk[h]]
+        got_v = [0 if m == 0 else (1 if m > 0 else 2) for m in mv[h]]
+        assert got_k == want_k and got_v == want_v, (h, held)
+        assert all(mk[h, i] > 0 and mv[h, i] > 0 for i in held)
+    if not held:
+        _same_cache(got, oracle.compress(d, K, V))
+    # the pools still hold what the modes say
+    Kt, Vt, _, keepK, keepV = pinlib.decode_cache(1, 2, 128, 16, 16, got)
+    assert (Kt == np.where(keepK, K, 0)).all() and (Vt == np.where(keepV, V, 0)).all()
+
+
+def test_dense_policy_rejects_counts_that_do_not_fit():
+    d = Dims(b=1, hkv=1, L=128, D=16, B=16, n_p=3, n_sk=3, n_sv=0)   # 6 ranked blocks needed
+    K = tie_heavy((1, 1, 128, 16), 73)
+    oracle.compress(d, K, K, sink=16, local=16)                      # 6 blocks left: fits
+    with pytest.raises(ValueError):
+        oracle.compress(d, K, K, sink=17, local=16)                  # 5 left
+    with pytest.raises(ValueError):
+        oracle.compress(d, K, K, sink=-1)
+
+
+# ------------------------------------------------------------------------------------------------
 # Re-compression ([HS] §III, Fig. 3): compress(unpack(cache), counts')
 
 def _same_cache(a, b):
