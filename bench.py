@@ -31,7 +31,7 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
-SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked", "policy")
+SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked", "policy", "f16")
 COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
 COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
 
@@ -61,8 +61,8 @@ def parse():
                    help="instead of the headline step: one JSON line per further workload; PARTS "
                         "is a comma list of " + ", ".join(SUITE_PARTS) + " (default: all): 16K "
                         "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, the "
-                        "prefill-to-decode re-compression, the caller-mask compressor and the "
-                        "sink/local dense policy at 32K batch 8")
+                        "prefill-to-decode re-compression, the caller-mask compressor, the "
+                        "sink/local dense policy and the fp16 element type at 32K batch 8")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -190,25 +190,26 @@ def summarize_counters(fetch_dir, write_dir):
 
 # ------------------------------------------------------------------------------------------------
 
-def make_inputs(w, torch, dev):
-    """Seeded N(0,1) bf16 K, V, prompt Q and decode q of the workload shape, drawn on the device
-    (torch's seeded generator; the timing does not depend on the values), with the workload's
-    key outlier channels scaled by 8."""
+def make_inputs(w, torch, dev, dtype=None):
+    """Seeded N(0,1) K, V, prompt Q and decode q of the workload shape (bf16, or the torch dtype
+    given), drawn on the device (torch's seeded generator; the timing does not depend on the
+    values), with the workload's key outlier channels scaled by 8."""
+    dtype = dtype or torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
     K = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
-    K = K.to(torch.bfloat16)
+    K = K.to(dtype)
     if w.outliers:
         for h in range(w.hkv):
             ch = torch.randperm(w.D, generator=g, device=dev)[:w.outliers]
             K[:, h, :, ch] *= 8
     V = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev,
-                    dtype=torch.float32).to(torch.bfloat16)
-    Q = torch.empty((w.b, w.hq, w.L, w.D), device=dev, dtype=torch.bfloat16)
+                    dtype=torch.float32).to(dtype)
+    Q = torch.empty((w.b, w.hq, w.L, w.D), device=dev, dtype=dtype)
     for bi in range(w.b):
         Q[bi] = torch.randn((w.hq, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
     q = torch.randn((w.b, w.hq, w.D), generator=g, device=dev, dtype=torch.float32)
-    return K, V, Q, q.to(torch.bfloat16)
+    return K, V, Q, q.to(dtype)
 
 
 def cpu_baseline(w, heads, min_seconds=10.0):
@@ -309,6 +310,8 @@ def run_suite(parts=SUITE_PARTS, reps=7):
         suite_masked(hs, synth, setup, timed, emit, torch)
     if "policy" in parts:
         suite_policy(hs, synth, setup, timed, decode_time, emit)
+    if "f16" in parts:
+        suite_f16(hs, synth, timed, decode_time, prefill_time, emit, torch)
     return 0
 
 
@@ -466,6 +469,39 @@ def suite_policy(hs, synth, setup, timed, decode_time, emit):
           "decode_us": round(t * 1e6, 2), "decode_bytes": nbytes,
           "decode_policy_gbs": round(nbytes / t_p / 1e9, 1)})
     del K, V, q, cache, cache_p
+
+def suite_f16(hs, synth, timed, decode_time, prefill_time, emit, torch):
+    """The 32K batch-8 workload in fp16 (the pages' precision): compressor, decode and causal
+    prefill on the sparse cache and on the all-dense cache, so that the speedups can be set beside
+    the pages' fp16 ratios."""
+    w = synth.workload("decode_llama8b_32k_b8")
+    G = w.hq // w.hkv
+    K, V, Q, q = make_inputs(w, torch, "cuda", torch.float16)
+    shp = hs.shape(w.b, w.hq, w.hkv, w.L, w.D, w.B, dtype=hs.HS_F16)
+    res = {}
+    for tag, counts in (("sparse", w.counts()), ("dense", (0, 0, 0))):
+        cnt = hs.counts(*counts)
+        cache = hs.alloc_cache(shp, cnt)
+        ws = hs.alloc_workspace(hs.HS_OP_COMPRESS, shp, cnt)
+        comp = timed(lambda: hs.hs_compress(shp, cnt, K, V, cache, ws))
+        t_d = decode_time(shp, cnt, cache, q)
+        t_p = prefill_time(shp, cnt, cache, Q, hs.HS_PREFILL_SMFMAC)
+        mk, mv = cache["map_k"].cpu().numpy(), cache["map_v"].cpu().numpy()
+        res[tag] = (comp, t_d, t_p, prefill_flops(w, mk, mv, True))
+        del cache
+    comp, t_d, t_p, (dense_eq, ex, _) = res["sparse"]
+    _, t_d0, t_p0, _ = res["dense"]
+    nbytes = decode_bytes(w, G)
+    emit({"suite": w.name + "_f16", "decode_us": round(t_d * 1e6, 2),
+          "decode_gbs": round(nbytes / t_d / 1e9, 1),
+          "frac_hbm_peak": round(nbytes / t_d / 1e9 / HBM_PEAK_GBS, 4),
+          "decode_dense_cache_us": round(t_d0 * 1e6, 2), "decode_speedup": round(t_d0 / t_d, 3),
+          "prefill_ms": round(t_p * 1e3, 3), "prefill_dense_cache_ms": round(t_p0 * 1e3, 3),
+          "prefill_speedup": round(t_p0 / t_p, 3),
+          "prefill_tflops_dense_equivalent": round(dense_eq / t_p / 1e12, 1),
+          "mfma_utilisation": round(ex / (BF16_DENSE_PEAK_TFLOPS * 1e12) / t_p, 4),
+          "compress_us": round(comp * 1e6, 1)})
+    del K, V, Q, q
 
 def main():
     args = parse()

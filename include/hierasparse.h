@@ -18,7 +18,8 @@
  *                    ([HS] §V-A).
  *
  * Conventions shared by every entry point
- *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
+ *   - bf16 or fp16 tensors (hs_shape.dtype) are passed as uint16_t bit patterns; all tensors are
+ *     dense row-major.
  *   - Every pointer except the size-query outputs is a DEVICE pointer owned by the caller. The
  *     library allocates no memory and keeps no state besides a thread-local error string.
  *   - Work is enqueued asynchronously on 'stream' (a hipStream_t; NULL = the default stream).
@@ -26,8 +27,8 @@
  *   - All arguments are validated on the host before anything is launched. On any error the
  *     call returns a non-zero hs_status, enqueues nothing, and hs_last_error() describes it.
  *     Faults inside a launched kernel surface at the caller's next synchronisation.
- *   - Inputs must be finite with |x| < 2^24 (the compressor's integer loss keys rely on it);
- *     this is documented, not checked.
+ *   - Inputs must be finite with |x| < 2^24 (the compressor's integer loss keys rely on it; every
+ *     finite fp16 value is); this is documented, not checked.
  *   - GPU limits: head_dim = 128, block in {64, 128}, seq_len % block = 0,
  *     seq_len / block <= 4096, q_heads % kv_heads = 0. Every pointer must be 16-byte aligned.
  *
@@ -88,7 +89,13 @@ typedef struct {
   int32_t seq_len;  /* tokens in the cache (decode) or in the prompt (prefill) */
   int32_t head_dim; /* D */
   int32_t block;    /* B, tokens per block */
+  int32_t dtype;    /* element type of K, V, Q and O: HS_BF16 (0) or HS_F16 (1) */
 } hs_shape;
+
+/* Element types. bf16 is the default; fp16 is the precision of [HS] §IV-A. The packed format,
+   the metadata and the block modes are the same for both (the 2:4 selection compares the 16-bit
+   magnitudes, which order both formats alike); loss keys are floor(|x| * 2^24) of the value. */
+enum { HS_BF16 = 0, HS_F16 = 1 };
 
 /* Block counts per (batch entry, KV head); the same for every head. */
 typedef struct {

@@ -6,8 +6,8 @@ this package; the GPU library and its Python binding never import it.
 What each function follows is cited in hso.c ("HieraSparse", arXiv 2604.16864v2: Eq. (1),
 Eq. (2a)-(2d), §III-B, §IV-A/B) together with the readings R1-R8 taken where the paper is silent;
 recompress (§III, Fig. 3) is the composition of unpack and compress (R9), compress_masked the
-generic compressor fed by caller masks (§III-A, §IV-B; R10), and compress(sink=, local=) the
-dense policy of the quality runs (§V-A; R11).
+generic compressor fed by caller masks (§III-A, §IV-B; R10), compress(sink=, local=) the dense
+policy of the quality runs (§V-A; R11), and Dims.dtype = 1 the fp16 element type (R12).
 Parity is pinned by the tests under tests/ (brute force, closed forms, library routines, identities).
 """
 import ctypes
@@ -25,7 +25,8 @@ _ERR = {1: "bad shape", 2: "bad block counts", 3: "input value non-finite or |x|
 
 
 class _Dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int) for n in ("b", "hkv", "L", "D", "B", "n_p", "n_sk", "n_sv")]
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("b", "hkv", "L", "D", "B", "n_p", "n_sk", "n_sv", "dtype")]
 
 
 def _lib():
@@ -40,7 +41,7 @@ def _lib():
         lib.hso_compress_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int, ctypes.c_int] + [P] * 12
         lib.hso_unpack.argtypes = [ctypes.POINTER(_Dims)] + [P] * 11
         lib.hso_compress_masked.argtypes = [ctypes.POINTER(_Dims)] + [P] * 13
-        lib.hso_attention.argtypes = [ctypes.c_int] * 8 + [P] * 4 + [ctypes.c_double,
+        lib.hso_attention.argtypes = [ctypes.c_int] * 9 + [P] * 4 + [ctypes.c_double,
                                                                       ctypes.c_int64, P, P, P]
         for f in (lib.hso_pool_elems, lib.hso_compress, lib.hso_unpack, lib.hso_attention,
                   lib.hso_compress_masked, lib.hso_compress_ex):
@@ -60,7 +61,8 @@ def _check(rc):
 
 @dataclass
 class Dims:
-    """b, Hkv, L tokens, head_dim D, block size B, and per-(batch, KV head) block counts."""
+    """b, Hkv, L tokens, head_dim D, block size B, per-(batch, KV head) block counts, and the
+    element type of the 16-bit patterns (0 bf16, 1 IEEE binary16; hso.c R12)."""
     b: int
     hkv: int
     L: int
@@ -69,13 +71,15 @@ class Dims:
     n_p: int
     n_sk: int
     n_sv: int
+    dtype: int = 0
 
     @property
     def nb(self):
         return self.L // self.B
 
     def c(self):
-        return _Dims(self.b, self.hkv, self.L, self.D, self.B, self.n_p, self.n_sk, self.n_sv)
+        return _Dims(self.b, self.hkv, self.L, self.D, self.B, self.n_p, self.n_sk, self.n_sv,
+                     self.dtype)
 
 
 POOLS = ("map_k", "map_v", "k_dense", "k_nnz", "k_meta", "v_dense", "v_nnz", "v_meta")
@@ -156,10 +160,11 @@ def recompress(d_in: Dims, cache: dict, d_out: Dims) -> dict:
     return compress(d_out, Kt, Vt)
 
 
-def attention(Q, Kt, Vt, visible, B: int, causal: bool, scale: float = 0.0, rows=None):
-    """fp64 softmax attention over visible tokens. Q [b][Hq][Lq][D] bf16 bits; Kt, Vt
-    [b][Hkv][L][D] bf16 bits; visible [b][Hkv][L/B]. rows: flat indices into [b][Hq][Lq] (None =
-    all). Returns (O [nrows][D] fp64, lse [nrows] fp64)."""
+def attention(Q, Kt, Vt, visible, B: int, causal: bool, scale: float = 0.0, rows=None,
+              dtype: int = 0):
+    """fp64 softmax attention over visible tokens. Q [b][Hq][Lq][D] 16-bit patterns of element type
+    dtype (0 bf16, 1 fp16); Kt, Vt [b][Hkv][L][D] likewise; visible [b][Hkv][L/B]. rows: flat
+    indices into [b][Hq][Lq] (None = all). Returns (O [nrows][D] fp64, lse [nrows] fp64)."""
     Q = np.ascontiguousarray(Q, dtype=np.uint16)
     Kt = np.ascontiguousarray(Kt, dtype=np.uint16)
     Vt = np.ascontiguousarray(Vt, dtype=np.uint16)
@@ -171,8 +176,9 @@ def attention(Q, Kt, Vt, visible, B: int, causal: bool, scale: float = 0.0, rows
     n = b * hq * lq if rows is None else len(rows)
     O = np.zeros((n, D), np.float64)
     lse = np.zeros(n, np.float64)
-    _check(_lib().hso_attention(b, hq, hkv, L, D, B, lq, int(causal), _ptr(Q), _ptr(Kt), _ptr(Vt),
-                                _ptr(visible), float(scale), n, _ptr(rows), _ptr(O), _ptr(lse)))
+    _check(_lib().hso_attention(b, hq, hkv, L, D, B, lq, int(causal), int(dtype), _ptr(Q),
+                                _ptr(Kt), _ptr(Vt), _ptr(visible), float(scale), n, _ptr(rows),
+                                _ptr(O), _ptr(lse)))
     return O, lse
 
 
@@ -180,10 +186,10 @@ def decode(d: Dims, cache: dict, q, hq: int, scale: float = 0.0, rows=None):
     """Decode attention over a compressed cache: q [b][Hq][D] -> (O, lse) for the listed rows."""
     Kt, Vt, vis = unpack(d, cache)
     q = np.asarray(q).reshape(d.b, hq, 1, d.D)
-    return attention(q, Kt, Vt, vis, d.B, False, scale, rows)
+    return attention(q, Kt, Vt, vis, d.B, False, scale, rows, d.dtype)
 
 
 def prefill(d: Dims, cache: dict, Q, scale: float = 0.0, rows=None):
     """Causal prefill attention over a compressed cache: Q [b][Hq][L][D]."""
     Kt, Vt, vis = unpack(d, cache)
-    return attention(Q, Kt, Vt, vis, d.B, True, scale, rows)
+    return attention(Q, Kt, Vt, vis, d.B, True, scale, rows, d.dtype)

@@ -46,6 +46,8 @@
  *   R11 dense policy ([HS] §V-A quality runs): a block holding any of the first 'sink' or the last
  *      'local' tokens stays dense for K and V and is not ranked; the counts select among the
  *      others.
+ *   R12 element type: K, V, Q are bf16 or IEEE binary16 ([HS] §IV-A computes in fp16) bit
+ *      patterns; the selection, the keys and the attention use the values they encode.
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,7 +61,7 @@
 #define HSO_ERR_MAP 4
 
 /* ------------------------------------------------------------------------------------------ */
-/* bf16 helpers                                                                                */
+/* Element values (R12): bf16 (dtype 0) or IEEE binary16 (dtype 1), as 16-bit patterns.        */
 
 static double bf16_value(uint16_t bits) {
   uint32_t w = (uint32_t)bits << 16;
@@ -68,13 +70,34 @@ static double bf16_value(uint16_t bits) {
   return (double)f;
 }
 
-/* R2: finite and |x| < 2^24 (exponent field at most 127 + 23). */
-static int bf16_in_range(uint16_t bits) { return ((bits & 0x7FFFu) >> 7) <= 150u; }
+/* binary16: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is subnormal. */
+static double f16_value(uint16_t bits) {
+  int e = (bits >> 10) & 31, m = bits & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + m, e - 25);
+  return (bits & 0x8000u) ? -v : v;
+}
+
+static double value(uint16_t bits, int dtype) { return dtype ? f16_value(bits) : bf16_value(bits); }
+
+/* R2: finite and |x| < 2^24 (bf16: exponent field at most 127 + 23; every finite fp16 value). */
+static int in_range(uint16_t bits, int dtype) {
+  if (dtype) return ((bits >> 10) & 31) != 31;
+  return ((bits & 0x7FFFu) >> 7) <= 150u;
+}
+static int is_finite(uint16_t bits, int dtype) {
+  return dtype ? (bits & 0x7C00u) != 0x7C00u : (bits & 0x7F80u) != 0x7F80u;
+}
 
 /* R2: the fixed-point magnitude floor(|x| * 2^24). |x| < 2^24 makes the product < 2^48, which a
    double holds exactly, so floor() of it is exact. */
-static uint64_t fixed_magnitude(uint16_t bits) {
-  return (uint64_t)floor(fabs(bf16_value(bits)) * 16777216.0);
+static uint64_t fixed_magnitude(uint16_t bits, int dtype) {
+  return (uint64_t)floor(fabs(value(bits, dtype)) * 16777216.0);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -83,6 +106,7 @@ static uint64_t fixed_magnitude(uint16_t bits) {
 typedef struct {
   int b, hkv, L, D, B;        /* batch, KV heads, tokens, head_dim, block size */
   int n_p, n_sk, n_sv;        /* per (batch, KV head): pruned, K 2:4, V 2:4 block counts */
+  int dtype;                  /* R12: 0 bf16, 1 fp16 */
 } hso_dims;
 
 static int dims_check(const hso_dims *d) {
@@ -119,13 +143,13 @@ int hso_pool_elems(const hso_dims *d, int64_t out[8]) {
 /* Keep the two largest |x| of a group of four; R1 for ties. Returns the kept positions with
    *i0 < *i1. A stable insertion sort by |x|, descending, leaves equal magnitudes in position
    order, so the first two entries are the kept pair. */
-static void keep_two(const uint16_t x[4], int *i0, int *i1) {
+static void keep_two(const uint16_t x[4], int dtype, int *i0, int *i1) {
   int order[4] = {0, 1, 2, 3};
   for (int p = 1; p < 4; ++p) {
     int j = order[p];
-    double mj = fabs(bf16_value(x[j]));
+    double mj = fabs(value(x[j], dtype));
     int q = p - 1;
-    while (q >= 0 && fabs(bf16_value(x[order[q]])) < mj) {
+    while (q >= 0 && fabs(value(x[order[q]], dtype)) < mj) {
       order[q + 1] = order[q];
       --q;
     }
@@ -136,12 +160,12 @@ static void keep_two(const uint16_t x[4], int *i0, int *i1) {
 }
 
 /* R10: the generic kernel's selection for a group the caller's element mask already thinned. */
-static void keep_nonzero(const uint16_t x[4], int *i0, int *i1) {
+static void keep_nonzero(const uint16_t x[4], int dtype, int *i0, int *i1) {
   int pos[4], n = 0;
   for (int j = 0; j < 4; ++j)
     if (x[j] & 0x7FFFu) pos[n++] = j;
   if (n > 2) {
-    keep_two(x, i0, i1);
+    keep_two(x, dtype, i0, i1);
     return;
   }
   for (int j = 0; j < 4 && n < 2; ++j)
@@ -150,7 +174,7 @@ static void keep_nonzero(const uint16_t x[4], int *i0, int *i1) {
   *i1 = pos[0] < pos[1] ? pos[1] : pos[0];
 }
 
-typedef void (*select_fn)(const uint16_t x[4], int *i0, int *i1);
+typedef void (*select_fn)(const uint16_t x[4], int dtype, int *i0, int *i1);
 
 /* The four elements of group g of block i, for K (4 consecutive channels of one token, row = the
    token within the block) or V (4 consecutive tokens of one channel, row = the channel). */
@@ -200,10 +224,10 @@ static void block_keys(const hso_dims *d, const uint16_t *Kh, const uint16_t *Vh
           uint16_t x[4];
           int i0, i1;
           gather_group(X, is_v, d->L, d->D, d->B, i, r, g, x);
-          keep_two(x, &i0, &i1);
+          keep_two(x, d->dtype, &i0, &i1);
           for (int j = 0; j < 4; ++j) {
-            uint64_t q = fixed_magnitude(x[j]);
-            double a = fabs(bf16_value(x[j]));
+            uint64_t q = fixed_magnitude(x[j], d->dtype);
+            double a = fabs(value(x[j], d->dtype));
             kp += q;
             fp += a;
             if (j != i0 && j != i1) {
@@ -258,7 +282,7 @@ static void pack_row(const uint16_t *X, int is_v, const hso_dims *d, int i, int 
     uint16_t x[4];
     int i0, i1;
     gather_group(X, is_v, d->L, d->D, d->B, i, row, g, x);
-    select(x, &i0, &i1);
+    select(x, d->dtype, &i0, &i1);
     nnz[2 * g] = x[i0];
     nnz[2 * g + 1] = x[i1];
     meta[g / 4] |= (uint16_t)((i0 | (i1 << 2)) << (4 * (g % 4)));
@@ -339,7 +363,7 @@ int hso_compress_ex(const hso_dims *d, int sink, int local, const uint16_t *K, c
   }
   const int64_t heads = (int64_t)d->b * d->hkv, per_head = (int64_t)d->L * d->D;
   for (int64_t e = 0; e < heads * per_head; ++e)
-    if (!bf16_in_range(K[e]) || !bf16_in_range(V[e])) {
+    if (!in_range(K[e], d->dtype) || !in_range(V[e], d->dtype)) {
       free(held);
       return HSO_ERR_VALUE;
     }
@@ -390,7 +414,7 @@ int hso_compress_masked(const hso_dims *d, const uint16_t *K, const uint16_t *V,
   if (rc) return rc;
   const int64_t heads = (int64_t)d->b * d->hkv, per_head = (int64_t)d->L * d->D;
   for (int64_t e = 0; e < heads * per_head; ++e)
-    if ((K[e] & 0x7F80u) == 0x7F80u || (V[e] & 0x7F80u) == 0x7F80u) return HSO_ERR_VALUE;
+    if (!is_finite(K[e], d->dtype) || !is_finite(V[e], d->dtype)) return HSO_ERR_VALUE;
 
   const int nb = d->L / d->B;
   for (int64_t hd = 0; hd < heads; ++hd) {
@@ -499,7 +523,7 @@ int hso_unpack(const hso_dims *d, const int32_t *map_k, const int32_t *map_v,
  * O [nrows][D] fp64; lse [nrows] = max + ln(sum of exp(s - max)), -inf for an empty row.
  * scale <= 0 selects 1/sqrt(D).
  */
-int hso_attention(int b, int hq, int hkv, int L, int D, int B, int Lq, int causal,
+int hso_attention(int b, int hq, int hkv, int L, int D, int B, int Lq, int causal, int dtype,
                   const uint16_t *Q, const uint16_t *Kt, const uint16_t *Vt,
                   const uint8_t *visible, double scale, int64_t nrows, const int64_t *rows,
                   double *O, double *lse) {
@@ -523,13 +547,13 @@ int hso_attention(int b, int hq, int hkv, int L, int D, int B, int Lq, int causa
       int64_t kvh = (int64_t)bi * hkv + hi / G;
       const uint16_t *Kh = Kt + kvh * (int64_t)L * D, *Vh = Vt + kvh * (int64_t)L * D;
       const uint8_t *vis = visible + kvh * nb;
-      for (int c = 0; c < D; ++c) q[c] = bf16_value(Q[id * D + c]);
+      for (int c = 0; c < D; ++c) q[c] = value(Q[id * D + c], dtype);
       int last = causal ? qi : L - 1;
       double m = -INFINITY;
       for (int t = 0; t <= last; ++t) {
         if (!vis[t / B]) continue;
         double acc = 0;
-        for (int c = 0; c < D; ++c) acc += q[c] * bf16_value(Kh[(int64_t)t * D + c]);
+        for (int c = 0; c < D; ++c) acc += q[c] * value(Kh[(int64_t)t * D + c], dtype);
         s[t] = acc * scale;
         if (s[t] > m) m = s[t];
       }
@@ -541,7 +565,7 @@ int hso_attention(int b, int hq, int hkv, int L, int D, int B, int Lq, int causa
         if (!vis[t / B]) continue;
         double w = exp(s[t] - m);
         l += w;
-        for (int c = 0; c < D; ++c) o[c] += w * bf16_value(Vh[(int64_t)t * D + c]);
+        for (int c = 0; c < D; ++c) o[c] += w * value(Vh[(int64_t)t * D + c], dtype);
       }
       for (int c = 0; c < D; ++c) o[c] /= l;
       lse[r] = m + log(l);

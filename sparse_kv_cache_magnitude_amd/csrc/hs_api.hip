@@ -40,6 +40,8 @@ hs_status make_dims(const hs_shape *s, const hs_counts *c, hs::Dims *d) {
     return fail(HS_ERR_SHAPE, "q_heads (%d) must be a multiple of kv_heads (%d)", s->q_heads,
                 s->kv_heads);
   if (s->head_dim != 128) return fail(HS_ERR_SHAPE, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->dtype != HS_BF16 && s->dtype != HS_F16)
+    return fail(HS_ERR_SHAPE, "dtype must be HS_BF16 or HS_F16 (got %d)", s->dtype);
   if (s->block != 64 && s->block != 128)
     return fail(HS_ERR_SHAPE, "block must be 64 or 128 (got %d)", s->block);
   if (s->seq_len % s->block)
@@ -68,6 +70,7 @@ hs_status make_dims(const hs_shape *s, const hs_counts *c, hs::Dims *d) {
   d->nsv = c->n_sparse_v;
   d->ndk = nb - c->n_pruned - c->n_sparse_k;
   d->ndv = nb - c->n_pruned - c->n_sparse_v;
+  d->dtype = s->dtype == HS_F16 ? hs::kF16 : hs::kBf16;
   return HS_OK;
 }
 

@@ -22,10 +22,27 @@ constexpr int kD = 128;  // head_dim handled on the GPU
 // ----------------------------------------------------------------------------------------------
 // k_score
 
+// floor(|x| * 2^24) of an fp16 magnitude (bits & 0x7FFF): a normal value is (1024 + m) *
+// 2^(e - 25), so the key is (1024 + m) shifted by e - 1; a subnormal one is m * 2^-24, key m.
+// Every fp16 value is a multiple of 2^-24, so the key is exact.
+__device__ __forceinline__ uint64_t fixed_mag_f16(uint32_t a) {
+  const uint32_t e = a >> 10, m = a & 0x3FFu;
+  return e ? (uint64_t)(m | 0x400u) << (e - 1) : (uint64_t)m;
+}
+template <class E>
+__device__ __forceinline__ uint64_t fixed_mag_e(uint32_t a) {
+  if constexpr (__is_same(E, _Float16))
+    return fixed_mag_f16(a);
+  else
+    return fixed_mag(a);
+}
+
+template <class E>
 __device__ __forceinline__ void score_group(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                             uint64_t &drop, uint64_t &all) {
   uint32_t a0 = x0 & 0x7FFFu, a1 = x1 & 0x7FFFu, a2 = x2 & 0x7FFFu, a3 = x3 & 0x7FFFu;
-  uint64_t f0 = fixed_mag(a0), f1 = fixed_mag(a1), f2 = fixed_mag(a2), f3 = fixed_mag(a3);
+  uint64_t f0 = fixed_mag_e<E>(a0), f1 = fixed_mag_e<E>(a1), f2 = fixed_mag_e<E>(a2),
+           f3 = fixed_mag_e<E>(a3);
   uint32_t keep = keep_mask(a0, a1, a2, a3);
   all += f0 + f1 + f2 + f3;
   drop += ((keep & 1u) ? 0ull : f0) + ((keep & 2u) ? 0ull : f1) + ((keep & 4u) ? 0ull : f2) +
@@ -38,29 +55,38 @@ __device__ __forceinline__ void score_group(uint32_t x0, uint32_t x1, uint32_t x
 // inputs become tiny normal values that truncate to 0, their floor as well. At or above 256 the
 // conversion saturates to 0xFFFFFFFF, above every in-range key (255 * 2^24 = 0xFF000000): the
 // caller detects that and redoes the block with score_group.
+// fp16: the value converted to fp32 and scaled by 2^24 is an integer, truncated exactly below
+// 256 (largest key floor(255.875 * 2^24) = 0xFFE00000) and saturated from 256 on.
+template <class E>
 __device__ __forceinline__ uint32_t fixed_mag_small(uint32_t a) {
-  return (uint32_t)__uint_as_float((a << 16) + (24u << 23));
+  if constexpr (__is_same(E, _Float16))
+    return (uint32_t)((float)__builtin_bit_cast(_Float16, (uint16_t)a) * 16777216.0f);
+  else
+    return (uint32_t)__uint_as_float((a << 16) + (24u << 23));
 }
 // The two dropped values of a group are its two smallest keys (the key is monotone in the
 // magnitude, and which of two equal magnitudes is dropped does not change the sum).
+template <class E>
 __device__ __forceinline__ void score_group_fast(uint32_t x0, uint32_t x1, uint32_t x2,
                                                  uint32_t x3, uint64_t &drop, uint64_t &all,
                                                  uint32_t &fmax) {
-  const uint32_t f0 = fixed_mag_small(x0 & 0x7FFFu), f1 = fixed_mag_small(x1 & 0x7FFFu);
-  const uint32_t f2 = fixed_mag_small(x2 & 0x7FFFu), f3 = fixed_mag_small(x3 & 0x7FFFu);
+  const uint32_t f0 = fixed_mag_small<E>(x0 & 0x7FFFu), f1 = fixed_mag_small<E>(x1 & 0x7FFFu);
+  const uint32_t f2 = fixed_mag_small<E>(x2 & 0x7FFFu), f3 = fixed_mag_small<E>(x3 & 0x7FFFu);
   const uint32_t l1 = min(f0, f1), h1 = max(f0, f1), l2 = min(f2, f3), h2 = max(f2, f3);
   all += ((uint64_t)f0 + f1) + ((uint64_t)f2 + f3);
   drop += (uint64_t)min(l1, l2) + min(max(l1, l2), min(h1, h2));
   fmax = max(fmax, max(h1, h2));
 }
-constexpr uint32_t kMaxSmallKey = 0xFF000000u;  // floor(255 * 2^24), the largest fast-path key
+// The largest fast-path key: floor(255 * 2^24) for bf16, floor(255.875 * 2^24) for fp16.
+template <class E>
+constexpr uint32_t kMaxSmallKey = __is_same(E, _Float16) ? 0xFFE00000u : 0xFF000000u;
 
 __device__ __forceinline__ uint32_t elem(const uint4 &v, int e) {
   uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-template <int B>
+template <int B, class E>
 __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
                                                const uint16_t *__restrict__ V,
                                                uint64_t *__restrict__ keys, int L) {
@@ -80,17 +106,17 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // K: groups of four channels of one token
-      score_group_fast(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk,
+      score_group_fast<E>(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk,
                        kp, fmax);
-      score_group_fast(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk,
+      score_group_fast<E>(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk,
                        kp, fmax);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)  // V: groups of four tokens of one channel
-      score_group_fast(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp,
+      score_group_fast<E>(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp,
                        fmax);
   }
-  if (__ballot(fmax > kMaxSmallKey) != 0) {
+  if (__ballot(fmax > kMaxSmallKey<E>) != 0) {
     // A magnitude of 256 or more in this wave's share: redo the share with the 64-bit keys.
     kk = kv = kp = 0;
     for (int g = tid >> 4; g < B / 4; g += 16) {
@@ -102,12 +128,12 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        score_group(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk, kp);
-        score_group(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk, kp);
+        score_group<E>(kr[r].x & 0xFFFFu, kr[r].x >> 16, kr[r].y & 0xFFFFu, kr[r].y >> 16, kk, kp);
+        score_group<E>(kr[r].z & 0xFFFFu, kr[r].z >> 16, kr[r].w & 0xFFFFu, kr[r].w >> 16, kk, kp);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        score_group(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp);
+        score_group<E>(elem(vr[0], e), elem(vr[1], e), elem(vr[2], e), elem(vr[3], e), kv, kp);
     }
   }
 #pragma unroll
@@ -334,10 +360,17 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ K,
 hipError_t launch_compress(const Dims &d, const uint16_t *k, const uint16_t *v, const CacheView &c,
                            uint64_t *keys, hipStream_t stream, int dense_lo, int dense_hi) {
   const dim3 grid(d.nb, d.b * d.hkv);
-  if (d.B == 64)
-    k_score<64><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
-  else
-    k_score<128><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+  if (d.dtype == kF16) {
+    if (d.B == 64)
+      k_score<64, _Float16><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+    else
+      k_score<128, _Float16><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+  } else {
+    if (d.B == 64)
+      k_score<64, __bf16><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+    else
+      k_score<128, __bf16><<<grid, 256, 0, stream>>>(k, v, keys, d.L);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_rank<<<d.b * d.hkv, kRankThreads, 0, stream>>>(keys, d.nb, d.np, d.nsk, d.nsv, dense_lo,

@@ -83,6 +83,7 @@ __device__ __forceinline__ void wait_tile(int n) {
 // Lane l owns channels 4 (l % 32) .. +3 and the splits of parity l / 32, four query heads at a
 // time. Padding entries (heads past ncol, splits past the end) read a valid row with weight 0, so
 // every load is unconditional and one round of loads covers four heads.
+template <class E>
 __device__ __forceinline__ void combine(const DecodeArgs &a, size_t row0, size_t orow0, int ncol,
                                         int lane) {
   const int S = a.splits, q4 = lane & 31, hh = lane >> 5;
@@ -151,15 +152,15 @@ __device__ __forceinline__ void combine(const DecodeArgs &a, size_t row0, size_t
       const size_t orow = orow0 + c0 + cc;
       if (hh == 0)
         *reinterpret_cast<uint2 *>(a.o + orow * kD + 4 * q4) =
-            make_uint2(pack_bf16x2(acc[cc][0] * inv, acc[cc][1] * inv),
-                       pack_bf16x2(acc[cc][2] * inv, acc[cc][3] * inv));
+            make_uint2(pack2<E>(acc[cc][0] * inv, acc[cc][1] * inv),
+                       pack2<E>(acc[cc][2] * inv, acc[cc][3] * inv));
       if (a.lse && lane == 0)
         a.lse[orow] = wsum[cc] > 0.f ? mx[cc] + __logf(wsum[cc]) : -INFINITY;
     }
   }
 }
 
-template <int B>
+template <int B, class E>
 __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsDec];
   const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            sacc[t] = mfma16(*reinterpret_cast<const uint4 *>(kl + rk[s] + 4096 * t), qr[s],
+            sacc[t] = mfma16<E>(*reinterpret_cast<const uint4 *>(kl + rk[s] + 4096 * t), qr[s],
                              sacc[t]);
       } else {
 #pragma unroll
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
           for (int c2 = 0; c2 < 2; ++c2) {
             const uint4 kv = *reinterpret_cast<const uint4 *>(kl + rkn[c2] + 2048 * t);
             const uint32_t ix = *reinterpret_cast<const uint16_t *>(kl + rkm + 256 * t + 8 * c2);
-            sacc[t] = smfmac16(kv, qr[2 * c2], qr[2 * c2 + 1], ix, sacc[t]);
+            sacc[t] = smfmac16<E>(kv, qr[2 * c2], qr[2 * c2 + 1], ix, sacc[t]);
           }
       }
 
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
         const float p2 = __builtin_amdgcn_exp2f(sacc[t][2] - m_new);
         const float p3 = __builtin_amdgcn_exp2f(sacc[t][3] - m_new);
         psum += (p0 + p1) + (p2 + p3);
-        pp[2 * t] = pack_bf16x2(p0, p1);
-        pp[2 * t + 1] = pack_bf16x2(p2, p3);
+        pp[2 * t] = pack2<E>(p0, p1);
+        pp[2 * t + 1] = pack2<E>(p2, p3);
       }
       l_run = l_run * alpha + psum;
 #pragma unroll
@@ -381,9 +382,9 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       if (mv0 > 0) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-          oacc[ct] = mfma16(*reinterpret_cast<const uint4 *>(kl + rvd[0] + 2048 * ct), plo,
+          oacc[ct] = mfma16<E>(*reinterpret_cast<const uint4 *>(kl + rvd[0] + 2048 * ct), plo,
                             oacc[ct]);
-          oacc[ct] = mfma16(*reinterpret_cast<const uint4 *>(kl + rvd[1] + 2048 * ct), phi,
+          oacc[ct] = mfma16<E>(*reinterpret_cast<const uint4 *>(kl + rvd[1] + 2048 * ct), phi,
                             oacc[ct]);
         }
       } else {
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
         for (int ct = 0; ct < 8; ++ct) {
           const uint4 vv = *reinterpret_cast<const uint4 *>(kl + rvn + 1024 * ct);
           const uint32_t ix = *reinterpret_cast<const uint16_t *>(kl + rvm + 128 * ct);
-          oacc[ct] = smfmac16(vv, plo, phi, ix, oacc[ct]);
+          oacc[ct] = smfmac16<E>(vv, plo, phi, ix, oacc[ct]);
         }
       }
       mk0 = mk1;
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   if (ticket != (uint32_t)(a.splits - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  combine(a, row0, (size_t)bi * a.hq + hq0, ncol, lane);
+  combine<E>(a, row0, (size_t)bi * a.hq + hq0, ncol, lane);
 }
 
 }  // namespace
@@ -444,10 +445,17 @@ hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, u
                scale_log2};
   const int col_groups = (d.G + 15) / 16;
   const dim3 grid(splits, d.hkv * col_groups, d.b);
-  if (d.B == 64)
-    k_decode_split<64><<<grid, 64, 0, stream>>>(a);
-  else
-    k_decode_split<128><<<grid, 64, 0, stream>>>(a);
+  if (d.dtype == kF16) {
+    if (d.B == 64)
+      k_decode_split<64, _Float16><<<grid, 64, 0, stream>>>(a);
+    else
+      k_decode_split<128, _Float16><<<grid, 64, 0, stream>>>(a);
+  } else {
+    if (d.B == 64)
+      k_decode_split<64, __bf16><<<grid, 64, 0, stream>>>(a);
+    else
+      k_decode_split<128, __bf16><<<grid, 64, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -23,38 +23,93 @@
 
 namespace hs {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+// Element types of K, V, Q and O: E = __bf16 (the default) or _Float16. The packed format, the
+// metadata and the 2:4 selection work on the 16-bit patterns and are the same for both; the
+// matrix-core instructions, the fp32 -> 16-bit conversions and the magnitude keys differ.
+template <class E> using vec2 = E __attribute__((ext_vector_type(2)));
+template <class E> using vec8 = E __attribute__((ext_vector_type(8)));
+template <class E> using vec16 = E __attribute__((ext_vector_type(16)));
+typedef vec8<__bf16> bf16x8;
+typedef vec16<__bf16> bf16x16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ bf16x16 as_bf16x16(uint4 lo, uint4 hi) {
+template <class E>
+__device__ __forceinline__ vec8<E> as8(uint4 v) { return __builtin_bit_cast(vec8<E>, v); }
+template <class E>
+__device__ __forceinline__ vec16<E> as16(uint4 lo, uint4 hi) {
   struct P {
     uint4 a, b;
   } p{lo, hi};
-  return __builtin_bit_cast(bf16x16, p);
+  return __builtin_bit_cast(vec16<E>, p);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return as8<__bf16>(v); }
+__device__ __forceinline__ bf16x16 as_bf16x16(uint4 lo, uint4 hi) { return as16<__bf16>(lo, hi); }
+
+// Matrix-core instructions by element type (same operand layouts for both).
+__device__ __forceinline__ f32x4 mma16x32(vec8<__bf16> a, vec8<__bf16> b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16x32(vec8<_Float16> a, vec8<_Float16> b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 smma16x64(vec8<__bf16> a, vec16<__bf16> b, f32x4 c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
+}
+__device__ __forceinline__ f32x4 smma16x64(vec8<_Float16> a, vec16<_Float16> b, f32x4 c,
+                                           int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, idx, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32x16(vec8<__bf16> a, vec8<__bf16> b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32x16(vec8<_Float16> a, vec8<_Float16> b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 smma32x32(vec8<__bf16> a, vec16<__bf16> b, f32x16 c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, 0);
+}
+__device__ __forceinline__ f32x16 smma32x32(vec8<_Float16> a, vec16<_Float16> b, f32x16 c,
+                                            int idx) {
+  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, 0);
 }
 
+template <class E = __bf16>
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  return mma16x32(as8<E>(a), as8<E>(b), c);
 }
 
-// 2:4 sparse A (8 kept bf16 of 16 logical k) times dense B (two 16x16x32 B operands).
+// 2:4 sparse A (8 kept values of 16 logical k) times dense B (two 16x16x32 B operands).
+template <class E = __bf16>
 __device__ __forceinline__ f32x4 smfmac16(uint4 a, uint4 b_lo, uint4 b_hi, uint32_t idx,
                                           f32x4 c) {
-  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b_lo, b_hi), c,
-                                                    (int)idx, 0, 0);
+  return smma16x64(as8<E>(a), as16<E>(b_lo, b_hi), c, (int)idx);
 }
 
-// Two fp32 -> packed bf16x2 (round to nearest even, one gfx950 v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+// Two fp32 -> two packed 16-bit values (round to nearest even: one gfx950 v_cvt_pk_bf16_f32 or
+// v_cvt_pk_f16_f32).
+template <class E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, vec2<E>));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return pack2<__bf16>(lo, hi); }
+
+// acc + x.lo + x.hi for two packed 16-bit values (one v_dot2 with ones).
+__device__ __forceinline__ float add_pair(vec2<__bf16> x, float acc) {
+  const vec2<__bf16> one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+__device__ __forceinline__ float add_pair(vec2<_Float16> x, float acc) {
+  const vec2<_Float16> one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(x, one, acc, false);
+}
+template <class E>
+__device__ __forceinline__ float add_pair_bits(uint32_t x, float acc) {
+  return add_pair(__builtin_bit_cast(vec2<E>, x), acc);
 }
 
 // ----------------------------------------------------------------------------------------------

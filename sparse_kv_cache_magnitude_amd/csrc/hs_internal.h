@@ -6,6 +6,7 @@
 namespace hs {
 
 constexpr int kMaxBlocks = 4096;  // blocks per head handled by the in-LDS ranking
+constexpr int kBf16 = 0, kF16 = 1;  // element types (hs_shape.dtype)
 
 // Validated problem description (see hs_api.hip).
 struct Dims {
@@ -13,6 +14,7 @@ struct Dims {
   int L, D, B, nb;    // tokens, head_dim, block size, blocks per head
   int np, nsk, nsv;   // per-head pruned / K 2:4 / V 2:4 block counts
   int ndk, ndv;       // per-head dense block counts
+  int dtype;          // kBf16 or kF16
 };
 
 struct CacheView {

@@ -71,8 +71,6 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 __device__ __forceinline__ int swap13(int x) { return (x & ~10) | ((x & 2) << 2) | ((x & 8) >> 2); }
@@ -82,14 +80,17 @@ __device__ __forceinline__ int swap13(int x) { return (x & ~10) | ((x & 2) << 2)
 __device__ __forceinline__ int tau(int r, bool split) { return split ? swap13(r) : swap23(r); }
 
 // ---- matrix-core helpers -----------------------------------------------------------------------
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+template <class E>
+__device__ __forceinline__ f32x16 mfma32(vec8<E> a, vec8<E> b, f32x16 c) {
+  return mma32x16(a, b, c);
 }
-__device__ __forceinline__ f32x16 smfmac32(bf16x8 a, bf16x16 b, uint32_t idx, f32x16 c) {
-  return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, (int)idx, 0, 0);
+template <class E>
+__device__ __forceinline__ f32x16 smfmac32(vec8<E> a, vec16<E> b, uint32_t idx, f32x16 c) {
+  return smma32x32(a, b, c, (int)idx);
 }
 // Half k of a 32-deep B operand pair: the B operand of one 16-deep dense step.
-__device__ __forceinline__ bf16x8 half8(bf16x16 v, int k2) {
+template <class E>
+__device__ __forceinline__ vec8<E> half8(vec16<E> v, int k2) {
   return k2 ? __builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15)
             : __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -107,9 +108,10 @@ __device__ __forceinline__ uint4 lds16(const char *p) { return *reinterpret_cast
 __device__ __forceinline__ uint2 lds8(const char *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 // Two packed 2:4 groups (4 kept values as two dwords, 8 metadata bits) -> 8 dense values.
-__device__ __forceinline__ bf16x8 expand2(uint2 v, uint32_t bits) {
+template <class E>
+__device__ __forceinline__ vec8<E> expand2(uint2 v, uint32_t bits) {
   const uint2 g0 = expand_group(v.x, bits & 15u), g1 = expand_group(v.y, (bits >> 4) & 15u);
-  return as_bf16x8(make_uint4(g0.x, g0.y, g1.x, g1.y));
+  return as8<E>(make_uint4(g0.x, g0.y, g1.x, g1.y));
 }
 
 // Combine a per-lane value of the two wave halves (lanes l and l ^ 32) with max / sum.
@@ -135,11 +137,12 @@ struct PrefillArgs {
 };
 
 // Per-wave state of the online softmax and the output accumulators (one 32-query tile).
+template <class E>
 struct WaveState {
-  bf16x16 qv[4];  // Q^T as GEMM1 B operand, per 32 channels (two 16-channel dense k-steps)
+  vec16<E> qv[4];  // Q^T as GEMM1 B operand, per 32 channels (two 16-channel dense k-steps)
   f32x16 o[4];    // O^T, per 32-channel tile
   f32x16 s[2];    // S^T of the current tile, per 32-token half
-  bf16x16 p[2];   // P^T per 32 tokens (two 16-token dense k-steps): previous tile until
+  vec16<E> p[2];  // P^T per 32 tokens (two 16-token dense k-steps): previous tile until
                   // overwritten by the current one
   float m_run, l_run, m_use, alpha;
 };
@@ -154,8 +157,8 @@ struct LaneOffsets {
 
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
 // Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
-template <bool kSparseK, bool kSmfmac>
-__device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOffsets &lo, int hf) {
+template <bool kSparseK, bool kSmfmac, class E>
+__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     f32x16 acc = zero16();
@@ -165,7 +168,7 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOf
       for (int ks = 0; ks < 8; ++ks) k[ks] = lds16(st + (lo.kd ^ (32 * ks)) + T * 8192);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        acc = mfma32(as_bf16x8(k[ks]), half8(w.qv[ks >> 1], ks & 1), acc);
+        acc = mfma32(as8<E>(k[ks]), half8<E>(w.qv[ks >> 1], ks & 1), acc);
     } else {
       const uint4 meta = lds16(st + lo.km + T * 512);
       const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
@@ -175,14 +178,14 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOf
         for (int u = 0; u < 4; ++u) k[u] = lds16(st + (lo.kn ^ (32 * u)) + T * 4096);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          acc = smfmac32(as_bf16x8(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
+          acc = smfmac32(as8<E>(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
       } else {
         // Decompress: the lane's 8-byte half of 16-byte unit ks.
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const uint32_t bits = (mw[ks >> 1] >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          acc = mfma32(expand2(lds8(st + (lo.knd ^ (16 * ks)) + T * 4096), bits),
-                       half8(w.qv[ks >> 1], ks & 1), acc);
+          acc = mfma32(expand2<E>(lds8(st + (lo.knd ^ (16 * ks)) + T * 4096), bits),
+                       half8<E>(w.qv[ks >> 1], ks & 1), acc);
         }
       }
     }
@@ -196,16 +199,17 @@ __device__ __forceinline__ void gemm1(WaveState &w, const char *st, const LaneOf
 // lane's tokens 0..7 at group positions {0,1}, index 0x4444), and for a dense tile a second one on
 // tokens 8..15 at positions {2,3} (index 0xEEEE). For a dense tile P^T arrives in the matching
 // token order (tau with bits 1 and 3 exchanged).
-__device__ __forceinline__ void gemm2_smfmac_step(WaveState &w, const char *st, bool sparse,
+template <class E>
+__device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *st, bool sparse,
                                                   const uint2 *meta, int u, const LaneOffsets &lo,
                                                   int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
     const uint32_t idx = sparse ? ((u ? meta[ct].y : meta[ct].x) >> (16 * hf)) : 0x4444u;
-    w.o[ct] = smfmac32(as_bf16x8(lds16(st + off + ct * kCtStride)), w.p[u], idx, w.o[ct]);
+    w.o[ct] = smfmac32(as8<E>(lds16(st + off + ct * kCtStride)), w.p[u], idx, w.o[ct]);
     if (!sparse)
-      w.o[ct] = smfmac32(as_bf16x8(lds16(st + (off ^ 16) + ct * kCtStride)), w.p[u], 0xEEEEu,
+      w.o[ct] = smfmac32(as8<E>(lds16(st + (off ^ 16) + ct * kCtStride)), w.p[u], 0xEEEEu,
                          w.o[ct]);
   }
 }
@@ -217,27 +221,28 @@ __device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool spa
 }
 
 // ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
-template <bool kSparseV>
-__device__ __forceinline__ void gemm2_dense_step(WaveState &w, const char *st, const uint2 *meta,
+template <bool kSparseV, class E>
+__device__ __forceinline__ void gemm2_dense_step(WaveState<E> &w, const char *st, const uint2 *meta,
                                                  int ks, const LaneOffsets &lo, int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    bf16x8 v;
+    vec8<E> v;
     if (!kSparseV) {
-      v = as_bf16x8(lds16(st + (lo.vdd ^ (32 * ks)) + ct * kCtStride));
+      v = as8<E>(lds16(st + (lo.vdd ^ (32 * ks)) + ct * kCtStride));
     } else {
       const uint32_t bits =
           (((ks >> 1) ? meta[ct].y : meta[ct].x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-      v = expand2(lds8(st + (lo.vnd ^ (16 * ks)) + ct * kCtStride), bits);
+      v = expand2<E>(lds8(st + (lo.vnd ^ (16 * ks)) + ct * kCtStride), bits);
     }
-    w.o[ct] = mfma32(v, half8(w.p[ks >> 1], ks & 1), w.o[ct]);
+    w.o[ct] = mfma32(v, half8<E>(w.p[ks >> 1], ks & 1), w.o[ct]);
   }
 }
 
 // ---- softmax of the current tile: causal mask, running max, decision to rescale ----------------
 // 'shift' = (first token of the key tile) - (first query of the wave); a token is masked when
 // shift + token > query. Returns true if the running max moves (then w.alpha rescales O and l).
-__device__ __forceinline__ bool softmax_max(WaveState &w, bool diag, bool split, int shift, int r,
+template <class E>
+__device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool split, int shift, int r,
                                             int hf, float c) {
   if (diag) {
 #pragma unroll
@@ -268,7 +273,8 @@ __device__ __forceinline__ bool softmax_max(WaveState &w, bool diag, bool split,
 // P^T of the current tile for GEMM2 k-step ks (16 tokens): the accumulator registers
 // 8*(ks&1) .. +7 of half ks>>1, exponentiated and packed to bf16. The bf16 values are also summed
 // (dot product with ones) into the running denominator.
-__device__ __forceinline__ void softmax_exp(WaveState &w, int ks, float c, float mc, float &lsum) {
+template <class E>
+__device__ __forceinline__ void softmax_exp(WaveState<E> &w, int ks, float c, float mc, float &lsum) {
   const f32x16 &s = w.s[ks >> 1];
   const int base = 8 * (ks & 1);
   uint32_t pk[4];
@@ -276,19 +282,19 @@ __device__ __forceinline__ void softmax_exp(WaveState &w, int ks, float c, float
   for (int e = 0; e < 4; ++e) {
     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e], c, -mc));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e + 1], c, -mc));
-    pk[e] = pack_bf16x2(p0, p1);
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), one, lsum, false);
+    pk[e] = pack2<E>(p0, p1);
+    lsum = add_pair_bits<E>(pk[e], lsum);
   }
-  const bf16x8 nw = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-  bf16x16 &pp = w.p[ks >> 1];
-  pp = (ks & 1) ? __builtin_shufflevector(half8(pp, 0), nw, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+  const vec8<E> nw = as8<E>(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  vec16<E> &pp = w.p[ks >> 1];
+  pp = (ks & 1) ? __builtin_shufflevector(half8<E>(pp, 0), nw, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
                                           12, 13, 14, 15)
-                : __builtin_shufflevector(nw, half8(pp, 1), 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                : __builtin_shufflevector(nw, half8<E>(pp, 1), 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
                                           12, 13, 14, 15);
 }
 
-__device__ __forceinline__ void softmax_finish(WaveState &w, bool need, float lsum) {
+template <class E>
+__device__ __forceinline__ void softmax_finish(WaveState<E> &w, bool need, float lsum) {
   if (need) {
     w.l_run = w.l_run * w.alpha + lsum;
 #pragma unroll
@@ -299,25 +305,25 @@ __device__ __forceinline__ void softmax_finish(WaveState &w, bool need, float ls
   }
 }
 
-template <bool kSmfmac>
-__device__ __forceinline__ void gemm2_u(WaveState &w, const char *st, bool sparse,
+template <bool kSmfmac, class E>
+__device__ __forceinline__ void gemm2_u(WaveState<E> &w, const char *st, bool sparse,
                                         const uint2 *meta, int u, const LaneOffsets &lo, int hf) {
   if (kSmfmac) {
     gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
   } else if (sparse) {
-    gemm2_dense_step<true>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<true>(w, st, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<true, E>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<true, E>(w, st, meta, 2 * u + 1, lo, hf);
   } else {
-    gemm2_dense_step<false>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<false>(w, st, meta, 2 * u + 1, lo, hf);
+    gemm2_dense_step<false, E>(w, st, meta, 2 * u, lo, hf);
+    gemm2_dense_step<false, E>(w, st, meta, 2 * u + 1, lo, hf);
   }
 }
 
 // Exponentials of the current tile interleaved with GEMM2 of the previous tile (if 'gemm'): the
 // instructions that read P^T of the previous tile are issued first, then the same registers
 // receive P^T of the current tile, 32 tokens at a time.
-template <bool kSmfmac>
-__device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev, bool gemm,
+template <bool kSmfmac, class E>
+__device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
                                                float c) {
   float lsum = 0.f;
@@ -339,7 +345,7 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState &w, const char *st_prev
 // by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves 3-6
 // (block 128, where a tile is half of each channel's metadata row).
 
-template <int B, bool kSmfmac>
+template <int B, bool kSmfmac, class E>
 __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hf = lane >> 5;
@@ -397,14 +403,14 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   }
   n_vis = __builtin_amdgcn_readfirstlane(n_vis);
 
-  WaveState w;
+  WaveState<E> w;
   {
     const uint16_t *qp =
         a.q + (((size_t)bi * a.hq + hq_i) * a.L + (size_t)kQTile * qt + r) * kD + 8 * hf;
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      w.qv[u] = as_bf16x16(has_task ? *reinterpret_cast<const uint4 *>(qp + 32 * u) : z,
+      w.qv[u] = as16<E>(has_task ? *reinterpret_cast<const uint4 *>(qp + 32 * u) : z,
                            has_task ? *reinterpret_cast<const uint4 *>(qp + 32 * u + 16) : z);
   }
   // Retire the Q loads here with a wait the compiler sees, so it never re-waits on them inside
@@ -564,20 +570,24 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x16 &acc = w.o[ct];
-      const uint2 v = make_uint2(pack_bf16x2(acc[4 * j] * inv, acc[4 * j + 1] * inv),
-                                 pack_bf16x2(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv));
+      const uint2 v = make_uint2(pack2<E>(acc[4 * j] * inv, acc[4 * j + 1] * inv),
+                                 pack2<E>(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv));
       *reinterpret_cast<uint2 *>(op + 32 * ct + 8 * j) = v;
     }
   if (a.lse && hf == 0) a.lse[qrow] = l > 0.f ? (w.m_run + log2f(l)) * kLn2 : -INFINITY;
 }
 
-template <int B>
+template <int B, class E>
 hipError_t launch_b(const PrefillArgs &a, bool smfmac, hipStream_t stream) {
   if (smfmac)
-    k_prefill<B, true><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+    k_prefill<B, true, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
   else
-    k_prefill<B, false><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+    k_prefill<B, false, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
+}
+template <class E>
+hipError_t launch_e(const PrefillArgs &a, int block, bool smfmac, hipStream_t stream) {
+  return block == 64 ? launch_b<64, E>(a, smfmac, stream) : launch_b<128, E>(a, smfmac, stream);
 }
 
 }  // namespace
@@ -602,7 +612,8 @@ hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, 
   a.ndv = d.ndv;
   a.nsv = d.nsv;
   a.scale_log2 = scale_log2;
-  return d.B == 64 ? launch_b<64>(a, smfmac, stream) : launch_b<128>(a, smfmac, stream);
+  return d.dtype == kF16 ? launch_e<_Float16>(a, d.B, smfmac, stream)
+                         : launch_e<__bf16>(a, d.B, smfmac, stream);
 }
 
 }  // namespace hs

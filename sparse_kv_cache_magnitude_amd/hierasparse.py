@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhieraspa
 HS_OK, HS_ERR_NULL, HS_ERR_SHAPE, HS_ERR_COUNTS, HS_ERR_ALIGN = 0, 1, 2, 3, 4
 HS_ERR_WORKSPACE, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_OVERLAP = 5, 6, 7, 8
 HS_OP_COMPRESS, HS_OP_DECODE, HS_OP_RECOMPRESS = 1, 2, 3
+HS_BF16, HS_F16 = 0, 1
 HS_PREFILL_SMFMAC, HS_PREFILL_DECOMPRESS = 0, 1
 
 EXPORTS = ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
@@ -26,7 +27,7 @@ CACHE_FIELDS = ("map_k", "map_v", "k_dense", "k_nnz", "k_meta", "v_dense", "v_nn
 
 class HsShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "q_heads", "kv_heads", "seq_len", "head_dim", "block")]
+                ("batch", "q_heads", "kv_heads", "seq_len", "head_dim", "block", "dtype")]
 
 
 class HsCounts(ctypes.Structure):
@@ -91,8 +92,8 @@ def _check(status):
         raise HsError(status, lib().hs_last_error().decode())
 
 
-def shape(batch, q_heads, kv_heads, seq_len, head_dim=128, block=64):
-    return HsShape(batch, q_heads, kv_heads, seq_len, head_dim, block)
+def shape(batch, q_heads, kv_heads, seq_len, head_dim=128, block=64, dtype=HS_BF16):
+    return HsShape(batch, q_heads, kv_heads, seq_len, head_dim, block, dtype)
 
 
 def counts(n_pruned, n_sparse_k, n_sparse_v):

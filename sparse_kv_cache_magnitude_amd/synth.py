@@ -27,37 +27,56 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), numpy's round to nearest even."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def to_bits(x: np.ndarray, dtype: int = 0) -> np.ndarray:
+    """float32 -> 16-bit patterns of element type dtype (0 bf16, 1 fp16)."""
+    return f16_bits(x) if dtype else bf16_bits(x)
+
+
+def to_f32(bits: np.ndarray, dtype: int = 0) -> np.ndarray:
+    return f16_to_f32(bits) if dtype else bf16_to_f32(bits)
+
+
 def _streams(seed: int):
     return [np.random.Generator(np.random.PCG64(s))
             for s in np.random.SeedSequence(seed).spawn(QKV_STREAMS)]
 
 
 def make_kv(seed: int, b: int, hkv: int, L: int, D: int, outliers: int = 0,
-            outlier_scale: float = 8.0):
-    """K, V [b][hkv][L][D] bf16 bits ~ N(0,1), drawn head by head. With outliers > 0, each KV head
-    gets that many distinct key channels (shared by every batch entry and token) scaled by
-    outlier_scale after rounding (a power of two, so exact in bf16)."""
+            outlier_scale: float = 8.0, dtype: int = 0):
+    """K, V [b][hkv][L][D] 16-bit patterns (dtype 0 bf16, 1 fp16) ~ N(0,1), drawn head by head.
+    With outliers > 0, each KV head gets that many distinct key channels (shared by every batch
+    entry and token) scaled by outlier_scale after rounding (a power of two, so exact)."""
     _, rk, rv, ro = _streams(seed)
     K = np.empty((b, hkv, L, D), np.uint16)
     V = np.empty((b, hkv, L, D), np.uint16)
     for bi in range(b):
         for h in range(hkv):
-            K[bi, h] = bf16_bits(rk.standard_normal((L, D), dtype=np.float32))
+            K[bi, h] = to_bits(rk.standard_normal((L, D), dtype=np.float32), dtype)
     for bi in range(b):
         for h in range(hkv):
-            V[bi, h] = bf16_bits(rv.standard_normal((L, D), dtype=np.float32))
+            V[bi, h] = to_bits(rv.standard_normal((L, D), dtype=np.float32), dtype)
     if outliers:
         for h in range(hkv):
             ch = ro.choice(D, outliers, replace=False)
             for c in ch:
-                K[:, h, :, c] = bf16_bits(bf16_to_f32(K[:, h, :, c]) * np.float32(outlier_scale))
+                K[:, h, :, c] = to_bits(to_f32(K[:, h, :, c], dtype) * np.float32(outlier_scale),
+                                        dtype)
     return K, V
 
 
-def make_q(seed: int, b: int, hq: int, lq: int, D: int):
-    """Q [b][hq][lq][D] bf16 bits ~ N(0,1) (lq = 1 for decode)."""
+def make_q(seed: int, b: int, hq: int, lq: int, D: int, dtype: int = 0):
+    """Q [b][hq][lq][D] 16-bit patterns (dtype 0 bf16, 1 fp16) ~ N(0,1) (lq = 1 for decode)."""
     rq = _streams(seed)[0]
-    return bf16_bits(rq.standard_normal((b, hq, lq, D), dtype=np.float32))
+    return to_bits(rq.standard_normal((b, hq, lq, D), dtype=np.float32), dtype)
 
 
 def random_modes(seed: int, b: int, hkv: int, nb: int, n_p: int, n_sk: int, n_sv: int):

@@ -9,28 +9,28 @@ from fractions import Fraction
 
 import numpy as np
 
-from sparse_kv_cache_magnitude_amd.synth import bf16_to_f32
+from sparse_kv_cache_magnitude_amd.synth import to_f32
 
 
-def mag(bits) -> Fraction:
-    """Exact |x| of one bf16 bit pattern."""
-    return Fraction(abs(float(bf16_to_f32(np.uint16(bits)))))
+def mag(bits, dtype=0) -> Fraction:
+    """Exact |x| of one 16-bit pattern (dtype 0 bf16, 1 fp16)."""
+    return Fraction(abs(float(to_f32(np.uint16(bits), dtype))))
 
 
-def kept_pair_brute(x4) -> tuple:
+def kept_pair_brute(x4, dtype=0) -> tuple:
     """The pair of positions whose magnitudes have the largest sum; among equal sums the
     lexicographically smallest pair (itertools.combinations yields pairs in that order)."""
     best, best_s = None, None
     for pair in itertools.combinations(range(4), 2):
-        s = mag(x4[pair[0]]) + mag(x4[pair[1]])
+        s = mag(x4[pair[0]], dtype) + mag(x4[pair[1]], dtype)
         if best is None or s > best_s:
             best, best_s = pair, s
     return best
 
 
-def fixed24(bits) -> int:
+def fixed24(bits, dtype=0) -> int:
     """floor(|x| * 2^24) in exact integer arithmetic."""
-    return math.floor(mag(bits) * (1 << 24))
+    return math.floor(mag(bits, dtype) * (1 << 24))
 
 
 def groups_of_block(X, is_v, B, D, i):
@@ -46,7 +46,7 @@ def groups_of_block(X, is_v, B, D, i):
                 yield c, g, blk[4 * g:4 * g + 4, c]
 
 
-def block_keys_exact(Kh, Vh, B, D):
+def block_keys_exact(Kh, Vh, B, D, dtype=0):
     """[nb][3] Python ints: K 2:4 loss, V 2:4 loss, whole-block loss (all of K and V)."""
     nb = Kh.shape[0] // B
     out = []
@@ -54,9 +54,9 @@ def block_keys_exact(Kh, Vh, B, D):
         k2 = v2 = p = 0
         for is_v, X in ((0, Kh), (1, Vh)):
             for _, _, x4 in groups_of_block(X, is_v, B, D, i):
-                keep = kept_pair_brute(x4)
+                keep = kept_pair_brute(x4, dtype)
                 for j in range(4):
-                    q = fixed24(x4[j])
+                    q = fixed24(x4[j], dtype)
                     p += q
                     if j not in keep:
                         if is_v:
@@ -149,12 +149,13 @@ def decode_cache(b, hkv, L, D, B, cache):
     return Kt, Vt, vis, keepK, keepV
 
 
-def attention_full_matrix(Q, Kt, Vt, vis, B, causal, scale=None):
+def attention_full_matrix(Q, Kt, Vt, vis, B, causal, scale=None, dtype=0):
     """Eq. (1) with the full score matrix materialised (no online softmax), fp64.
-    Q [b][hq][lq][D]; Kt, Vt [b][hkv][L][D] bf16 bits; returns O [b][hq][lq][D], lse."""
-    q = bf16_to_f32(Q).astype(np.float64)
-    k = bf16_to_f32(Kt).astype(np.float64)
-    v = bf16_to_f32(Vt).astype(np.float64)
+    Q [b][hq][lq][D]; Kt, Vt [b][hkv][L][D] 16-bit patterns (dtype 0 bf16, 1 fp16); returns
+    O [b][hq][lq][D], lse."""
+    q = to_f32(Q, dtype).astype(np.float64)
+    k = to_f32(Kt, dtype).astype(np.float64)
+    v = to_f32(Vt, dtype).astype(np.float64)
     b, hq, lq, D = q.shape
     hkv, L = k.shape[1], k.shape[2]
     G = hq // hkv

@@ -74,6 +74,7 @@ def _status(call):
 BAD_SHAPES = [
     (hs.shape(1, 4, 1, 1024, 64, 64), hs.HS_ERR_SHAPE),       # head_dim != 128
     (hs.shape(1, 4, 1, 1024, 128, 32), hs.HS_ERR_SHAPE),      # block not 64/128
+    (hs.shape(1, 4, 1, 1024, 128, 64, dtype=2), hs.HS_ERR_SHAPE),  # unknown element type
     (hs.shape(1, 4, 1, 1000, 128, 64), hs.HS_ERR_SHAPE),      # seq_len % block
     (hs.shape(1, 6, 4, 1024, 128, 64), hs.HS_ERR_SHAPE),      # q_heads % kv_heads
     (hs.shape(0, 4, 1, 1024, 128, 64), hs.HS_ERR_SHAPE),      # empty batch

@@ -176,6 +176,86 @@ def test_round_trip_and_map_is_a_bijection():
 
 
 # ------------------------------------------------------------------------------------------------
+# fp16 element type (hso.c R12; [HS] §IV-A computes in fp16)
+
+def f16_normal(shape, seed):
+    return synth.f16_bits(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))
+
+
+def test_f16_values_match_numpy_for_every_pattern():
+    """Attention over one visible token returns that token's V row exactly, so every finite fp16
+    pattern passes through the oracle's decoding once and must equal numpy's float16 value."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = bits[(bits & 0x7C00) != 0x7C00]                   # 63488 patterns
+    L = -(-len(finite) // 128)
+    V = np.zeros(L * 128, np.uint16)
+    V[:len(finite)] = finite
+    V = V.reshape(1, 1, L, 128)                                 # one token per 128 patterns
+    K = np.zeros_like(V)
+    Q = np.zeros((1, 1, 1, 128), np.uint16)
+    for t in range(L):
+        vis = np.zeros((1, 1, L), np.uint8)                     # block size 1: token t alone
+        vis[0, 0, t] = 1
+        O, _ = oracle.attention(Q, K, V, vis, 1, False, dtype=1)
+        assert np.array_equal(O[0], V[0, 0, t].view(np.float16).astype(np.float64)), t
+
+
+def test_f16_kept_pairs_and_keys_exact():
+    d = Dims(b=1, hkv=2, L=64, D=16, B=16, n_p=1, n_sk=1, n_sv=2, dtype=1)
+    vals = np.array([0.0, -0.0, 6e-8, -6e-8, 1e-5, 0.5, -0.5, 3.0, 65504.0, -1000.0],
+                    np.float32)
+    rng = np.random.default_rng(81)
+    K = synth.f16_bits(vals[rng.integers(0, len(vals), (1, 2, 64, 16))])
+    V = f16_normal((1, 2, 64, 16), 82)
+    V[0, 1, 5, 3] = synth.f16_bits(np.float32(6e-8))          # subnormal: key 1
+    out = oracle.compress(d, K, V, with_loss=True)
+    _, _, _, keepK, keepV = pinlib.decode_cache(1, 2, 64, 16, 16, out)
+    for h in range(2):
+        want = pinlib.block_keys_exact(K[0, h], V[0, h], 16, 16, dtype=1)
+        assert [tuple(int(x) for x in r) for r in out["keys"][0, h]] == want
+        keys = [tuple(int(x) for x in r) for r in out["keys"][0, h]]
+        mk = out["map_k"].reshape(2, 4)[h]
+        mv = out["map_v"].reshape(2, 4)[h]
+        wk, wv = pinlib.modes_brute(keys, 1, 1, 2)
+        assert [0 if m == 0 else (1 if m > 0 else 2) for m in mk] == wk
+        assert [0 if m == 0 else (1 if m > 0 else 2) for m in mv] == wv
+        for is_v, X, keep in ((0, K[0, h], keepK[0, h]), (1, V[0, h], keepV[0, h])):
+            m = mv if is_v else mk
+            for i in range(4):
+                if m[i] >= 0:
+                    continue
+                for row, g, x4 in pinlib.groups_of_block(X, is_v, 16, 16, i):
+                    got = (keep[i * 16 + row, 4 * g:4 * g + 4] if not is_v
+                           else keep[i * 16 + 4 * g:i * 16 + 4 * g + 4, row])
+                    assert tuple(np.flatnonzero(got)) == pinlib.kept_pair_brute(x4, 1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f16_sparsity_zero_equals_library_attention(causal):
+    B, L, D = 16, 64, 32
+    d = Dims(b=1, hkv=2, L=L, D=D, B=B, n_p=0, n_sk=0, n_sv=0, dtype=1)
+    K, V = f16_normal((1, 2, L, D), 83), f16_normal((1, 2, L, D), 84)
+    Q = f16_normal((1, 4, L, D), 85)
+    cache = oracle.compress(d, K, V)
+    o, _ = oracle.prefill(d, cache, Q) if causal else oracle.attention(
+        Q, *oracle.unpack(d, cache), B, False, dtype=1)
+    f = lambda a: torch.from_numpy(a.view(np.float16).astype(np.float64))
+    kq = f(K).repeat_interleave(2, dim=1)
+    vq = f(V).repeat_interleave(2, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(f(Q), kq, vq, is_causal=causal)
+    np.testing.assert_allclose(o.reshape(ref.shape), ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_f16_rejects_non_finite():
+    d = Dims(b=1, hkv=1, L=16, D=16, B=16, n_p=0, n_sk=1, n_sv=0, dtype=1)
+    K = np.zeros((1, 1, 16, 16), np.uint16)
+    oracle.compress(d, K, K)
+    K[0, 0, 3, 3] = 0x7C00                                       # +inf
+    with pytest.raises(ValueError):
+        oracle.compress(d, K, np.zeros_like(K))
+
+
+# ------------------------------------------------------------------------------------------------
 # Dense policy of the quality runs ([HS] §V-A): sink and local-window blocks stay dense
 
 @pytest.mark.parametrize("sink,local", [(0, 0), (1, 0), (16, 0), (17, 40), (0, 16), (0, 33),
