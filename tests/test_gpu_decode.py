@@ -162,3 +162,24 @@ def test_decode_workspace_reuse():
         ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
         assert_close(synth.bf16_to_f32(gu.to_host_u16(o)), ref, lse.cpu().numpy(), ref_lse,
                      f"reuse b={b} hq={hq} B={B} splits={splits}")
+
+
+@pytest.mark.parametrize("B,L,counts,splits", [
+    (64, 64 * 40, (0, 40, 40), 0),          # every block 2:4
+    (64, 64 * 40, (13, 27, 27), 7),         # 2:4 and pruned blocks only
+    (128, 128 * 21, (5, 16, 16), 0),
+    (128, 128 * 21, (5, 16, 16), 64),       # splits with a single tile or none
+    (64, 64 * 3, (2, 1, 1), 0),             # one visible block
+    (64, 64 * 2048, (300, 1748, 1748), 3),  # more blocks than one listing pass holds
+])
+def test_decode_2to4_only_cache(B, L, counts, splits):
+    """Caches without a dense block (every visible block 2:4 for K and V)."""
+    rng = np.random.default_rng(L + splits)
+    b, hq, hkv = (1, 4, 1) if L > 100000 else (2, 8, 2)
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
+    print(f"[decode 2:4 only] B={B} L={L} counts={counts} splits={splits}", flush=True)
+    o, lse, cache = run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=splits)
+    ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
+    assert_close(o, ref, lse, ref_lse, f"2:4 only B={B} {counts} s={splits}")

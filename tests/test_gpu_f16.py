@@ -80,7 +80,8 @@ def run_decode_f16(b, hq, hkv, L, B, counts, K, V, q):
     return synth.f16_to_f32(gu.to_host_u16(o)), lse.cpu().numpy(), ref, ref_lse
 
 
-@pytest.mark.parametrize("B,counts", [(64, (5, 20, 11)), (128, (2, 9, 14)), (64, (0, 0, 0))])
+@pytest.mark.parametrize("B,counts", [(64, (5, 20, 11)), (128, (2, 9, 14)), (64, (0, 0, 0)),
+                                      (64, (4, 28, 28)), (128, (3, 29, 29))])
 def test_f16_decode_small(B, counts):
     rng = np.random.default_rng(B + 1)
     b, hq, hkv, L = 2, 8, 2, 32 * B
