@@ -66,6 +66,21 @@ template <int B>
 __device__ __forceinline__ int tile_loads(int mk, int mv) {
   return (mk > 0 ? 16 : 9) + (mv > 0 ? 16 : (B == 64 ? 9 : 12));
 }
+// Inclusive prefix sum of x over the 64 lanes of the wave, on DPP lane moves (no LDS round trips):
+// Hillis-Steele steps of 1, 2, 4, 8 lanes inside each 16-lane row (a lane whose source lies before
+// its row adds 0), then each row adds the totals of the rows before it: lane 15's sum goes to row
+// 1 (and lane 47's to row 3), then lane 31's to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 2, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 4, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 8, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xC, 0xF, false);
+  return x;
+}
+
 // Wait until at most n vector-memory operations are outstanding (n = a tile_loads value).
 __device__ __forceinline__ void wait_tile(int n) {
   switch (n) {
@@ -262,11 +277,13 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   // of kScanChunks 64-block chunks at a time, in passes of at most kListCap entries.
   const int32_t *mkh = a.c.map_k + (size_t)head * a.nb;
   const int32_t *mvh = a.c.map_v + (size_t)head * a.nb;
-  const int64_t two_w = 2 * (int64_t)a.total_w;
-  const int64_t lo_key = two_w * split, hi_key = two_w * (split + 1);
+  // Keys fit in 32 bits: w <= 2 tiles x 32 loads per block and nb <= 4096 give total_w <= 2^18,
+  // and splits <= 512, so 2 * total_w * splits <= 2^28.
+  const int two_w = 2 * a.total_w;
+  const int lo_key = two_w * split, hi_key = two_w * (split + 1);
   const bool last_split = split == a.splits - 1;
   int scan = 0;       // first block of the next chunk
-  int64_t base = 0;   // sum of w over the blocks before 'scan'
+  int base = 0;       // sum of w over the blocks before 'scan'
   bool finished = a.total_w <= 0;
   while (!finished) {
     int got = 0;  // blocks listed in this pass
@@ -282,13 +299,8 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
       for (int i = 0; i < kScanChunks; ++i) {
         if (finished) break;
         const int w = mkv[i] != 0 ? TPB * tile_loads<B>(mkv[i], mvv[i]) : 0;
-        int incl = w;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        const int64_t key = (2 * (base + incl - w) + w) * (int64_t)a.splits;
+        const int incl = wave_incl_scan(w);
+        const int key = (2 * (base + incl - w) + w) * a.splits;
         const bool mine = w > 0 && key >= lo_key && (key < hi_key || last_split);
         const uint64_t bal = __ballot(mine);
         if (mine) {
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
           lv[r] = mvv[i];
         }
         got += __popcll(bal);
-        base += __shfl(incl, 63, 64);
+        base += __builtin_amdgcn_readlane(incl, 63);
         scan += 64;
         // keys grow with the block index: once one passes this split's share, the rest do too
         const bool past = !last_split && __ballot(w > 0 && key >= hi_key) != 0;
