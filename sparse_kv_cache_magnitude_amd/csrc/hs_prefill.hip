@@ -30,8 +30,10 @@
 // registers per 32-token half); P^T needs no data movement between lanes. The stage stores the K
 // rows already in that order.
 // SMFMAC path: 2:4 operands go to v_smfmac; dense V^T is fed to the same instruction as two 2:4
-// halves (so the output accumulators see one instruction type). Decompress path: 2:4 operands are
-// expanded in registers from the same LDS stage and everything runs on dense MFMA.
+// halves (so the output accumulators see one instruction type). Decompress path: after a tile has
+// landed, the whole workgroup expands its 2:4 operands once into a dense scratch tile in LDS (the
+// dense stage layout; one more barrier), and GEMM1, the softmax and GEMM2 of that tile then run on
+// dense MFMA without the one-tile GEMM2 lag.
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -66,8 +68,12 @@ constexpr int kListModesOff = kStages * kStageBytes;
 constexpr int kListBlkOff = kListModesOff + 4 * kMaxBlocks;
 constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
 constexpr int kLdsBytes = kCountOff + 4 * kWaves;  // 120 KB
+// Decompress path: the dense image of the current tile's 2:4 operands (the stage layout, K at 0,
+// V^T at kRegion), expanded once per tile by the whole workgroup.
+constexpr int kScratchOff = (kLdsBytes + 1023) / 1024 * 1024;
+constexpr int kLdsDecomp = kScratchOff + kStageBytes;  // 153 KB
 static_assert(kRegion / 1024 == 2 * kWaves && kMetaOff / 1024 == kWaves, "loads per wave");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kLdsBytes <= 160 * 1024 && kLdsDecomp <= 160 * 1024, "LDS budget");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -339,6 +345,38 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
   return lsum;
 }
 
+// ---- decompress path: 2:4 operands of a stage expanded into the dense stage layout -------------
+// Dense K row slot r holds at 16-byte unit j the channels 8c .. 8c + 7, c = j ^ (r & 15); the 2:4
+// K row keeps their eight values (groups 2c, 2c + 1) in half c & 1 of its unit c >> 1, found at
+// unit (c >> 1) ^ ((r >> 1) & 7), and their metadata in byte c of the row's 16 metadata bytes.
+// Dense V^T channel row ch holds at unit j the tokens 8t .. 8t + 7, t = j ^ ((ch >> 1) & 7); the
+// 2:4 V^T row (32-row group ch / 32, row ch % 32) keeps them in half t & 1 of unit t >> 1, found
+// at unit (t >> 1) ^ ((ch >> 2) & 3), with metadata byte t of the channel's 8 bytes. Each of the
+// workgroup's 512 lanes expands two K units and two V units.
+template <class E>
+__device__ __forceinline__ void expand_tile(const char *st, char *dst, bool sparse_k, bool sparse_v,
+                                            int tid) {
+  if (sparse_k) {
+#pragma unroll
+    for (int i = tid; i < 64 * 16; i += kWaves * 64) {
+      const int r = i >> 4, j = i & 15, c = j ^ (r & 15);
+      const uint2 kv = lds8(st + r * 128 + 16 * ((c >> 1) ^ ((r >> 1) & 7)) + 8 * (c & 1));
+      const uint32_t bits = *reinterpret_cast<const uint8_t *>(st + kMetaOff + r * 16 + c);
+      *reinterpret_cast<vec8<E> *>(dst + r * 256 + 16 * j) = expand2<E>(kv, bits);
+    }
+  }
+  if (sparse_v) {
+#pragma unroll
+    for (int i = tid; i < 128 * 8; i += kWaves * 64) {
+      const int ch = i >> 3, j = i & 7, t = j ^ ((ch >> 1) & 7);
+      const int row = kRegion + (ch >> 5) * kCtStride + (ch & 31) * 64;
+      const uint2 vv = lds8(st + row + 16 * ((t >> 1) ^ ((ch >> 2) & 3)) + 8 * (t & 1));
+      const uint32_t bits = *reinterpret_cast<const uint8_t *>(st + kVMetaOff + ch * 8 + t);
+      *reinterpret_cast<vec8<E> *>(dst + kRegion + ch * 128 + 16 * j) = expand2<E>(vv, bits);
+    }
+  }
+}
+
 // ---- staging of one tile -----------------------------------------------------------------------
 // Each region is a whole number of 1 KB loads (64 lanes x 16 B); load q of a region goes to wave
 // q % 8, so a wave issues two loads for a dense region and one for 2:4 values. Metadata: K (1 KB)
@@ -347,7 +385,7 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
 
 template <int B, bool kSmfmac, class E>
 __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[kSmfmac ? kLdsBytes : kLdsDecomp];
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int TPB = B / kTile;  // 64-token tiles per block
@@ -522,6 +560,44 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
 
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
   // own queries are fully masked by the causal test and contribute nothing.
+  if constexpr (!kSmfmac) {
+    // Decompress path: each tile's 2:4 operands are expanded once into the dense scratch tile
+    // (one more barrier), then GEMM1, the softmax and GEMM2 of the tile run on dense operands.
+    char *scratch = lds + kScratchOff;
+    int stage = 0;
+    for (int it = 0; it < n_tiles; ++it) {
+      int kt1 = 0, mk1 = 0, mv1 = 0;
+      const bool more = it + 1 < n_tiles;
+      if (more) tile_info(it + 1, kt1, mk1, mv1);
+      const int next_stage = stage == kStages - 1 ? 0 : stage + 1;
+      wait_vmem(0);  // this wave's loads of tile it have landed
+      barrier();     // ... and every wave's; the scratch tile of tile it - 1 is no longer read
+      if (more) issue(kt1, mk1, mv1, next_stage);
+
+      const char *st = lds + stage * kStageBytes;
+      const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
+      if (sparse_k || sparse_v) {
+        expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      gemm1<false, false>(w, sparse_k ? scratch : st, lo, hf);
+      const int shift = kTile * kt0 - kQTile * qt;
+      const bool need = softmax_max(w, shift > -kTile, false, shift, r, hf, c);
+      const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
+      float lsum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
+      softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
+      const uint2 meta[4] = {};
+      const char *vb = sparse_v ? scratch : st;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) gemm2_dense_step<false, E>(w, vb, meta, ks, lo, hf);
+      stage = next_stage;
+      kt0 = kt1;
+      mk0 = mk1;
+      mv0 = mv1;
+    }
+  } else {
   bool prev_sparse_v = false;
   const char *st_prev = lds;
   int stage = 0;
@@ -557,6 +633,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     load_vmeta(meta, st_prev, prev_sparse_v, lo);
 #pragma unroll
     for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
+  }
   }
 
   if (!has_task) return;
