@@ -67,7 +67,11 @@ constexpr int kVMetaOff = kRegion + 2048;  // stage: 2:4 V metadata
 constexpr int kListModesOff = kStages * kStageBytes;
 constexpr int kListBlkOff = kListModesOff + 4 * kMaxBlocks;
 constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
-constexpr int kLdsBytes = kCountOff + 4 * kWaves;  // 120 KB
+// SMFMAC path: 1 KB of the index word a dense V^T tile's first SMFMAC uses (0x4444, positions 0
+// and 1 of every group), laid out like a stage's V^T metadata, so dense and 2:4 tiles read their
+// index words the same way.
+constexpr int kDenseIdxOff = (kCountOff + 4 * kWaves + 15) / 16 * 16;
+constexpr int kLdsBytes = kDenseIdxOff + 1024;  // 121 KB
 // Decompress path: the dense image of the current tile's 2:4 operands (the stage layout, K at 0,
 // V^T at kRegion), expanded once per tile by the whole workgroup.
 constexpr int kScratchOff = (kLdsBytes + 1023) / 1024 * 1024;
@@ -212,18 +216,19 @@ __device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *s
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
-    const uint32_t idx = sparse ? ((u ? meta[ct].y : meta[ct].x) >> (16 * hf)) : 0x4444u;
+    const uint32_t idx = (u ? meta[ct].y : meta[ct].x) >> (16 * hf);
     w.o[ct] = smfmac32(as8<E>(lds16(st + off + ct * kCtStride)), w.p[u], idx, w.o[ct]);
     if (!sparse)
       w.o[ct] = smfmac32(as8<E>(lds16(st + (off ^ 16) + ct * kCtStride)), w.p[u], 0xEEEEu,
                          w.o[ct]);
   }
 }
+// Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (kDenseIdxOff).
 __device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
-                                           const LaneOffsets &lo) {
+                                           const LaneOffsets &lo, const char *lds) {
+  const char *base = sparse ? st : lds + kDenseIdxOff - kVMetaOff;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-    meta[ct] = sparse ? lds8(st + lo.vm + ct * 32 * 8) : make_uint2(0, 0);
+  for (int ct = 0; ct < 4; ++ct) meta[ct] = lds8(base + lo.vm + ct * 32 * 8);
 }
 
 // ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
@@ -331,11 +336,11 @@ __device__ __forceinline__ void gemm2_u(WaveState<E> &w, const char *st, bool sp
 template <bool kSmfmac, class E>
 __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
-                                               float c) {
+                                               float c, const char *lds) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
   uint2 meta[4];
-  load_vmeta(meta, st_prev, gemm && sparse, lo);
+  load_vmeta(meta, st_prev, gemm && sparse, lo, lds);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (gemm) gemm2_u<kSmfmac>(w, st_prev, sparse, meta, u, lo, hf);
@@ -412,6 +417,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   int32_t *lmodes = reinterpret_cast<int32_t *>(lds + kListModesOff);
   int16_t *lblk = reinterpret_cast<int16_t *>(lds + kListBlkOff);
   int32_t *wcount = reinterpret_cast<int32_t *>(lds + kCountOff);
+  if (kSmfmac && tid < 256) reinterpret_cast<uint32_t *>(lds + kDenseIdxOff)[tid] = 0x44444444u;
   int n_vis = 0;
   {
     const int32_t *mkh = a.c.map_k + (size_t)head * a.nb, *mvh = a.c.map_v + (size_t)head * a.nb;
@@ -618,7 +624,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
       gemm1<false, kSmfmac>(w, st, lo, hf);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
-    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c);
+    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
     st_prev = st;
@@ -630,7 +636,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   // GEMM2 of the last tile (its stage is not overwritten after the loop).
   if (n_tiles > 0) {
     uint2 meta[4];
-    load_vmeta(meta, st_prev, prev_sparse_v, lo);
+    load_vmeta(meta, st_prev, prev_sparse_v, lo, lds);
 #pragma unroll
     for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
   }
