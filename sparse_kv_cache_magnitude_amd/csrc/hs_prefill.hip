@@ -71,7 +71,10 @@ constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
 // and 1 of every group), laid out like a stage's V^T metadata, so dense and 2:4 tiles read their
 // index words the same way.
 constexpr int kDenseIdxOff = (kCountOff + 4 * kWaves + 15) / 16 * 16;
-constexpr int kLdsBytes = kDenseIdxOff + 1024;  // 121 KB
+// SMFMAC path: 128 zero bytes. An SMFMAC accumulates in place, so the S^T accumulators of a 2:4 K
+// tile start from zeros read here (LDS broadcast reads) rather than from 16 VALU moves per half.
+constexpr int kZeroOff = kDenseIdxOff + 1024;
+constexpr int kLdsBytes = kZeroOff + 128;  // 121 KB
 // Decompress path: the dense image of the current tile's 2:4 operands (the stage layout, K at 0,
 // V^T at kRegion), expanded once per tile by the whole workgroup.
 constexpr int kScratchOff = (kLdsBytes + 1023) / 1024 * 1024;
@@ -168,10 +171,13 @@ struct LaneOffsets {
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
 // Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
 template <bool kSparseK, bool kSmfmac, class E>
-__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf) {
+__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf,
+                                      const char *lds) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    f32x16 acc = zero16();
+    f32x16 acc = (kSparseK && kSmfmac)
+                     ? *reinterpret_cast<const f32x16 *>(lds + kZeroOff + 64 * T)
+                     : zero16();
     if (!kSparseK) {
       uint4 k[8];  // all reads issued before the first MFMA that needs them
 #pragma unroll
@@ -418,6 +424,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   int16_t *lblk = reinterpret_cast<int16_t *>(lds + kListBlkOff);
   int32_t *wcount = reinterpret_cast<int32_t *>(lds + kCountOff);
   if (kSmfmac && tid < 256) reinterpret_cast<uint32_t *>(lds + kDenseIdxOff)[tid] = 0x44444444u;
+  if (kSmfmac && tid < 32) reinterpret_cast<uint32_t *>(lds + kZeroOff)[tid] = 0u;
   int n_vis = 0;
   {
     const int32_t *mkh = a.c.map_k + (size_t)head * a.nb, *mvh = a.c.map_v + (size_t)head * a.nb;
@@ -586,7 +593,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
         expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      gemm1<false, false>(w, sparse_k ? scratch : st, lo, hf);
+      gemm1<false, false>(w, sparse_k ? scratch : st, lo, hf, lds);
       const int shift = kTile * kt0 - kQTile * qt;
       const bool need = softmax_max(w, shift > -kTile, false, shift, r, hf, c);
       const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
@@ -619,9 +626,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     const char *st = lds + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
-      gemm1<true, kSmfmac>(w, st, lo, hf);
+      gemm1<true, kSmfmac>(w, st, lo, hf, lds);
     else
-      gemm1<false, kSmfmac>(w, st, lo, hf);
+      gemm1<false, kSmfmac>(w, st, lo, hf, lds);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
     const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
