@@ -210,23 +210,30 @@ __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const Lan
 }
 
 // ---- GEMM2 on the SMFMAC path, one 32-token k-step u ------------------------------------------
-// Dense and 2:4 V^T tiles share one instruction sequence, so O^T stays in one register set: per
+// Dense and 2:4 V^T tiles share one instruction type, so O^T stays in one register set: per
 // 32-channel tile, one SMFMAC on the kept values (2:4: stored values and metadata; dense: the
 // lane's tokens 0..7 at group positions {0,1}, index 0x4444), and for a dense tile a second one on
 // tokens 8..15 at positions {2,3} (index 0xEEEE). For a dense tile P^T arrives in the matching
-// token order (tau with bits 1 and 3 exchanged).
+// token order (tau with bits 1 and 3 exchanged). All operand reads of the k-step are issued before
+// its first SMFMAC, so their LDS latency is paid once. The tile-kind test stays next to each second
+// SMFMAC: one branch around the whole sequence makes the compiler copy the accumulators at the join.
 template <class E>
 __device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *st, bool sparse,
                                                   const uint2 *meta, int u, const LaneOffsets &lo,
                                                   int hf) {
+  const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
+  uint4 v0[4], v1[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) v0[ct] = lds16(st + off + ct * kCtStride);
+  if (!sparse) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) v1[ct] = lds16(st + (off ^ 16) + ct * kCtStride);
+  }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
     const uint32_t idx = (u ? meta[ct].y : meta[ct].x) >> (16 * hf);
-    w.o[ct] = smfmac32(as8<E>(lds16(st + off + ct * kCtStride)), w.p[u], idx, w.o[ct]);
-    if (!sparse)
-      w.o[ct] = smfmac32(as8<E>(lds16(st + (off ^ 16) + ct * kCtStride)), w.p[u], 0xEEEEu,
-                         w.o[ct]);
+    w.o[ct] = smfmac32(as8<E>(v0[ct]), w.p[u], idx, w.o[ct]);
+    if (!sparse) w.o[ct] = smfmac32(as8<E>(v1[ct]), w.p[u], 0xEEEEu, w.o[ct]);
   }
 }
 // Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (kDenseIdxOff).
