@@ -68,12 +68,15 @@ __device__ __forceinline__ f32x16 mma32x16(vec8<__bf16> a, vec8<__bf16> b, f32x1
 __device__ __forceinline__ f32x16 mma32x16(vec8<_Float16> a, vec8<_Float16> b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// kSet selects the 16-bit index set of the index word: 0 = bits [15:0], 1 = bits [31:16].
+template <int kSet = 0>
 __device__ __forceinline__ f32x16 smma32x32(vec8<__bf16> a, vec16<__bf16> b, f32x16 c, int idx) {
-  return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, 0);
+  return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, kSet);
 }
+template <int kSet = 0>
 __device__ __forceinline__ f32x16 smma32x32(vec8<_Float16> a, vec16<_Float16> b, f32x16 c,
                                             int idx) {
-  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, 0);
+  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, kSet);
 }
 
 template <class E = __bf16>

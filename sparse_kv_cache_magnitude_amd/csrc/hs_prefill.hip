@@ -97,9 +97,9 @@ template <class E>
 __device__ __forceinline__ f32x16 mfma32(vec8<E> a, vec8<E> b, f32x16 c) {
   return mma32x16(a, b, c);
 }
-template <class E>
+template <class E, int kSet = 0>
 __device__ __forceinline__ f32x16 smfmac32(vec8<E> a, vec16<E> b, uint32_t idx, f32x16 c) {
-  return smma32x32(a, b, c, (int)idx);
+  return smma32x32<kSet>(a, b, c, (int)idx);
 }
 // Half k of a 32-deep B operand pair: the B operand of one 16-deep dense step.
 template <class E>
@@ -152,7 +152,8 @@ struct PrefillArgs {
 // Per-wave state of the online softmax and the output accumulators (one 32-query tile).
 template <class E>
 struct WaveState {
-  vec16<E> qv[4];  // Q^T as GEMM1 B operand, per 32 channels (two 16-channel dense k-steps)
+  vec16<E> qv[4];  // Q^T as GEMM1 B operand: qv[s] holds channel chunks s and s + 4 (16 channels
+                   // each), i.e. the dense k-steps over chunks s and s + 4 back to back
   f32x16 o[4];    // O^T, per 32-channel tile
   f32x16 s[2];    // S^T of the current tile, per 32-token half
   vec16<E> p[2];  // P^T per 32 tokens (two 16-token dense k-steps): previous tile until
@@ -164,46 +165,39 @@ struct WaveState {
 // the unit swizzle folded in; a read XORs in the (compile-time) unit of its k-step and adds the
 // row-group offset.
 struct LaneOffsets {
-  int kd, kn, knd, km;  // dense K; 2:4 K values for SMFMAC (16 B) and decompress (8 B); metadata
-  int vd, vdd, vn, vnd, vm;  // dense V^T split (SMFMAC) and dense (decompress); 2:4 V^T; metadata
+  int kd, kn, km;       // dense K; 2:4 K values (16 B); 2:4 K metadata (8 B)
+  int vd, vdd, vn, vm;  // dense V^T split (SMFMAC) and dense (decompress); 2:4 V^T; metadata
 };
 
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
-// Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order.
-template <bool kSparseK, bool kSmfmac, class E>
-__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf,
+// Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order. The dense
+// k-step over 16-channel chunk cc takes the Q registers half8(qv[cc & 3], cc >> 2). The 2:4 step s
+// covers chunks s and s + 4: lane half hf holds the kept values of chunk s + 4hf, whose 16-bit
+// metadata word is half s & 1 of dword (s >> 1) + 2hf of the row's metadata. Each lane reads the two
+// dwords of its half once, and every SMFMAC selects its index set by the instruction's key, so no
+// per-lane shift of the metadata is needed.
+template <bool kSparseK, class E>
+__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo,
                                       const char *lds) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    f32x16 acc = (kSparseK && kSmfmac)
-                     ? *reinterpret_cast<const f32x16 *>(lds + kZeroOff + 64 * T)
-                     : zero16();
+    f32x16 acc = kSparseK ? *reinterpret_cast<const f32x16 *>(lds + kZeroOff + 64 * T) : zero16();
     if (!kSparseK) {
       uint4 k[8];  // all reads issued before the first MFMA that needs them
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) k[ks] = lds16(st + (lo.kd ^ (32 * ks)) + T * 8192);
+      for (int cc = 0; cc < 8; ++cc) k[cc] = lds16(st + (lo.kd ^ (32 * cc)) + T * 8192);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc = mfma32(as8<E>(k[ks]), half8<E>(w.qv[ks >> 1], ks & 1), acc);
+      for (int cc = 0; cc < 8; ++cc)
+        acc = mfma32(as8<E>(k[cc]), half8<E>(w.qv[cc & 3], cc >> 2), acc);
     } else {
-      const uint4 meta = lds16(st + lo.km + T * 512);
-      const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
-      if (kSmfmac) {
-        uint4 k[4];
+      const uint2 meta = lds8(st + lo.km + T * 512);
+      uint4 k[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) k[u] = lds16(st + (lo.kn ^ (32 * u)) + T * 4096);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc = smfmac32(as8<E>(k[u]), w.qv[u], mw[u] >> (16 * hf), acc);
-      } else {
-        // Decompress: the lane's 8-byte half of 16-byte unit ks.
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint32_t bits = (mw[ks >> 1] >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-          acc = mfma32(expand2<E>(lds8(st + (lo.knd ^ (16 * ks)) + T * 4096), bits),
-                       half8<E>(w.qv[ks >> 1], ks & 1), acc);
-        }
-      }
+      for (int s = 0; s < 4; ++s) k[s] = lds16(st + (lo.kn ^ (16 * s)) + T * 4096);
+      acc = smfmac32<E, 0>(as8<E>(k[0]), w.qv[0], meta.x, acc);
+      acc = smfmac32<E, 1>(as8<E>(k[1]), w.qv[1], meta.x, acc);
+      acc = smfmac32<E, 0>(as8<E>(k[2]), w.qv[2], meta.y, acc);
+      acc = smfmac32<E, 1>(as8<E>(k[3]), w.qv[3], meta.y, acc);
     }
     w.s[T] = acc;
   }
@@ -244,20 +238,13 @@ __device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool spa
   for (int ct = 0; ct < 4; ++ct) meta[ct] = lds8(base + lo.vm + ct * 32 * 8);
 }
 
-// ---- GEMM2 on the decompress path, one 16-token k-step ks --------------------------------------
-template <bool kSparseV, class E>
-__device__ __forceinline__ void gemm2_dense_step(WaveState<E> &w, const char *st, const uint2 *meta,
-                                                 int ks, const LaneOffsets &lo, int hf) {
+// ---- GEMM2 on the decompress path (dense operands), one 16-token k-step ks --------------------
+template <class E>
+__device__ __forceinline__ void gemm2_dense_step(WaveState<E> &w, const char *st, int ks,
+                                                 const LaneOffsets &lo) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    vec8<E> v;
-    if (!kSparseV) {
-      v = as8<E>(lds16(st + (lo.vdd ^ (32 * ks)) + ct * kCtStride));
-    } else {
-      const uint32_t bits =
-          (((ks >> 1) ? meta[ct].y : meta[ct].x) >> (16 * (ks & 1) + 8 * hf)) & 0xFFu;
-      v = expand2<E>(lds8(st + (lo.vnd ^ (16 * ks)) + ct * kCtStride), bits);
-    }
+    const vec8<E> v = as8<E>(lds16(st + (lo.vdd ^ (32 * ks)) + ct * kCtStride));
     w.o[ct] = mfma32(v, half8<E>(w.p[ks >> 1], ks & 1), w.o[ct]);
   }
 }
@@ -329,24 +316,10 @@ __device__ __forceinline__ void softmax_finish(WaveState<E> &w, bool need, float
   }
 }
 
-template <bool kSmfmac, class E>
-__device__ __forceinline__ void gemm2_u(WaveState<E> &w, const char *st, bool sparse,
-                                        const uint2 *meta, int u, const LaneOffsets &lo, int hf) {
-  if (kSmfmac) {
-    gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
-  } else if (sparse) {
-    gemm2_dense_step<true, E>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<true, E>(w, st, meta, 2 * u + 1, lo, hf);
-  } else {
-    gemm2_dense_step<false, E>(w, st, meta, 2 * u, lo, hf);
-    gemm2_dense_step<false, E>(w, st, meta, 2 * u + 1, lo, hf);
-  }
-}
-
 // Exponentials of the current tile interleaved with GEMM2 of the previous tile (if 'gemm'): the
 // instructions that read P^T of the previous tile are issued first, then the same registers
 // receive P^T of the current tile, 32 tokens at a time.
-template <bool kSmfmac, class E>
+template <class E>
 __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
                                                float c, const char *lds) {
@@ -356,7 +329,7 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
   load_vmeta(meta, st_prev, gemm && sparse, lo, lds);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (gemm) gemm2_u<kSmfmac>(w, st_prev, sparse, meta, u, lo, hf);
+    if (gemm) gemm2_smfmac_step(w, st_prev, sparse, meta, u, lo, hf);
     softmax_exp(w, 2 * u, c, mc, lsum);
     softmax_exp(w, 2 * u + 1, c, mc, lsum);
   }
@@ -468,8 +441,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      w.qv[u] = as16<E>(has_task ? *reinterpret_cast<const uint4 *>(qp + 32 * u) : z,
-                           has_task ? *reinterpret_cast<const uint4 *>(qp + 32 * u + 16) : z);
+      w.qv[u] = as16<E>(has_task ? *reinterpret_cast<const uint4 *>(qp + 16 * u) : z,
+                           has_task ? *reinterpret_cast<const uint4 *>(qp + 16 * u + 64) : z);
   }
   // Retire the Q loads here with a wait the compiler sees, so it never re-waits on them inside
   // the loop (where its vmcnt count would also drain the in-flight K/V prefetch).
@@ -483,13 +456,11 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   {
     const int f16 = r & 15, f8 = (r >> 1) & 7, f4 = (r >> 2) & 3;
     lo.kd = r * 256 + 32 * (f16 >> 1) + 16 * (hf ^ (f16 & 1));
-    lo.kn = r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
-    lo.knd = r * 128 + 16 * f8 + 8 * hf;
-    lo.km = kMetaOff + r * 16;
+    lo.kn = r * 128 + 16 * ((4 * hf) ^ f8);
+    lo.km = kMetaOff + r * 16 + 8 * hf;
     lo.vd = kRegion + r * 128 + 16 * ((2 * hf) ^ f8);
     lo.vdd = kRegion + r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
     lo.vn = kRegion + r * 64 + 32 * (f4 >> 1) + 16 * (hf ^ (f4 & 1));
-    lo.vnd = kRegion + r * 64 + 16 * f4 + 8 * hf;
     lo.vm = kVMetaOff + r * 8;
   }
 
@@ -600,7 +571,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
         expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      gemm1<false, false>(w, sparse_k ? scratch : st, lo, hf, lds);
+      gemm1<false>(w, sparse_k ? scratch : st, lo, lds);
       const int shift = kTile * kt0 - kQTile * qt;
       const bool need = softmax_max(w, shift > -kTile, false, shift, r, hf, c);
       const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
@@ -608,10 +579,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
       softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
-      const uint2 meta[4] = {};
       const char *vb = sparse_v ? scratch : st;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) gemm2_dense_step<false, E>(w, vb, meta, ks, lo, hf);
+      for (int ks = 0; ks < 4; ++ks) gemm2_dense_step<E>(w, vb, ks, lo);
       stage = next_stage;
       kt0 = kt1;
       mk0 = mk1;
@@ -633,12 +603,12 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     const char *st = lds + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
-      gemm1<true, kSmfmac>(w, st, lo, hf, lds);
+      gemm1<true>(w, st, lo, lds);
     else
-      gemm1<false, kSmfmac>(w, st, lo, hf, lds);
+      gemm1<false>(w, st, lo, lds);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
-    const float lsum = exp_and_gemm2<kSmfmac>(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
+    const float lsum = exp_and_gemm2(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
     softmax_finish(w, need, lsum);
     prev_sparse_v = sparse_v;
     st_prev = st;
@@ -652,7 +622,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     uint2 meta[4];
     load_vmeta(meta, st_prev, prev_sparse_v, lo, lds);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) gemm2_u<kSmfmac>(w, st_prev, prev_sparse_v, meta, u, lo, hf);
+    for (int u = 0; u < 2; ++u) gemm2_smfmac_step(w, st_prev, prev_sparse_v, meta, u, lo, hf);
   }
   }
 
