@@ -165,7 +165,7 @@ struct WaveState {
 // the unit swizzle folded in; a read XORs in the (compile-time) unit of its k-step and adds the
 // row-group offset.
 struct LaneOffsets {
-  int kd, kn, km;       // dense K; 2:4 K values (16 B); 2:4 K metadata (8 B)
+  int kd, kn, km;       // dense K; 2:4 K values; 2:4 K metadata (16 B each)
   int vd, vdd, vn, vm;  // dense V^T split (SMFMAC) and dense (decompress); 2:4 V^T; metadata
 };
 
@@ -173,11 +173,12 @@ struct LaneOffsets {
 // Lane (r, hf) reads row slot 32T + r; the stage holds the K rows in GEMM1 row order. The dense
 // k-step over 16-channel chunk cc takes the Q registers half8(qv[cc & 3], cc >> 2). The 2:4 step s
 // covers chunks s and s + 4: lane half hf holds the kept values of chunk s + 4hf, whose 16-bit
-// metadata word is half s & 1 of dword (s >> 1) + 2hf of the row's metadata. Each lane reads the two
-// dwords of its half once, and every SMFMAC selects its index set by the instruction's key, so no
-// per-lane shift of the metadata is needed.
+// metadata word is half s & 1 of dword (s >> 1) + 2hf of the row's metadata. Each lane reads the
+// row's 16 metadata bytes once (16 consecutive rows fill the 64 banks), keeps the two dwords of its
+// half, and every SMFMAC selects its index set by the instruction's key, so no per-lane shift of
+// the metadata is needed.
 template <bool kSparseK, class E>
-__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo,
+__device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf,
                                       const char *lds) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
@@ -190,7 +191,8 @@ __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const Lan
       for (int cc = 0; cc < 8; ++cc)
         acc = mfma32(as8<E>(k[cc]), half8<E>(w.qv[cc & 3], cc >> 2), acc);
     } else {
-      const uint2 meta = lds8(st + lo.km + T * 512);
+      const uint4 m4 = lds16(st + lo.km + T * 512);
+      const uint2 meta = hf ? make_uint2(m4.z, m4.w) : make_uint2(m4.x, m4.y);
       uint4 k[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) k[s] = lds16(st + (lo.kn ^ (16 * s)) + T * 4096);
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     const int f16 = r & 15, f8 = (r >> 1) & 7, f4 = (r >> 2) & 3;
     lo.kd = r * 256 + 32 * (f16 >> 1) + 16 * (hf ^ (f16 & 1));
     lo.kn = r * 128 + 16 * ((4 * hf) ^ f8);
-    lo.km = kMetaOff + r * 16 + 8 * hf;
+    lo.km = kMetaOff + r * 16;
     lo.vd = kRegion + r * 128 + 16 * ((2 * hf) ^ f8);
     lo.vdd = kRegion + r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
     lo.vn = kRegion + r * 64 + 32 * (f4 >> 1) + 16 * (hf ^ (f4 & 1));
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
         expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      gemm1<false>(w, sparse_k ? scratch : st, lo, lds);
+      gemm1<false>(w, sparse_k ? scratch : st, lo, hf, lds);
       const int shift = kTile * kt0 - kQTile * qt;
       const bool need = softmax_max(w, shift > -kTile, false, shift, r, hf, c);
       const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
@@ -603,9 +605,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     const char *st = lds + stage * kStageBytes;
     const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
     if (sparse_k)
-      gemm1<true>(w, st, lo, lds);
+      gemm1<true>(w, st, lo, hf, lds);
     else
-      gemm1<false>(w, st, lo, lds);
+      gemm1<false>(w, st, lo, hf, lds);
     const int shift = kTile * kt0 - kQTile * qt;
     const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
     const float lsum = exp_and_gemm2(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
