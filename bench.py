@@ -63,6 +63,11 @@ def parse():
                         "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, the "
                         "prefill-to-decode re-compression, the caller-mask compressor, the "
                         "sink/local dense policy and the fp16 element type at 32K batch 8")
+    p.add_argument("--peaks", action="store_true",
+                   help="instead of the headline step: the measured ceilings of the GPU "
+                        "(libhspeaks.so): matrix-core issue loops (MFMA and SMFMAC), vector-ALU "
+                        "loops (exp2, FMA, max3, bf16 pack), matrix-core and vector work sharing "
+                        "a SIMD, and streaming HBM reads; one JSON line each")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                         "then WRITE_SIZE, each with --copy-probe) into profiles/traffic.json")
@@ -506,10 +511,130 @@ def suite_f16(hs, synth, timed, decode_time, prefill_time, emit, torch):
           "compress_us": round(comp * 1e6, 1)})
     del K, V, Q, q
 
+def run_peaks(reps=3):
+    """Measured ceilings of the GPU. Each probe is timed with HIP events (median of `reps` after
+    one warm-up launch); cycle counts are per SIMD at the shader clock the probe's own clock
+    samples give (s_memtime against the 100 MHz counter). Every loop kernel runs one workgroup
+    per CU, so w waves per workgroup put w/4 waves on each of the 1024 SIMDs."""
+    import numpy as np
+    import torch
+    from sparse_kv_cache_magnitude_amd import peaks as pk
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    n_simd = 1024
+    out = torch.empty(1024 * 1024, device=dev, dtype=torch.float32)
+    clk = torch.zeros(4, device=dev, dtype=torch.int64)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return float(np.median(ts[1:]))
+
+    def clock_hz():
+        c = clk.cpu().numpy().astype(np.float64)
+        return (c[2] - c[0]) / max(c[3] - c[1], 1.0) * 1e8
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    grid = 1024  # four waves of workgroups over the 256 CUs
+    flops = {pk.HSP_MFMA_32X32X16: 32768, pk.HSP_SMFMAC_32X32X32: 65536,
+             pk.HSP_MFMA_16X16X32: 16384, pk.HSP_SMFMAC_16X16X64: 32768}
+    names = {pk.HSP_MFMA_32X32X16: "v_mfma_f32_32x32x16_bf16",
+             pk.HSP_SMFMAC_32X32X32: "v_smfmac_f32_32x32x32_bf16",
+             pk.HSP_MFMA_16X16X32: "v_mfma_f32_16x16x32_bf16",
+             pk.HSP_SMFMAC_16X16X64: "v_smfmac_f32_16x16x64_bf16"}
+    iters = 4096
+    f_clk = None
+    for kind in names:
+        for waves in (4, 8):
+            t = timed(lambda: pk.matrix_loop(kind, grid, waves, iters, out, clk))
+            f_clk = clock_hz()
+            n_ins = grid * waves * iters * 4
+            logical = n_ins * flops[kind]
+            sparse = kind in (pk.HSP_SMFMAC_32X32X32, pk.HSP_SMFMAC_16X16X64)
+            emit({"peak": "matrix_loop", "instruction": names[kind], "waves_per_simd": waves // 4,
+                  "ms": round(t * 1e3, 4), "shader_clock_ghz": round(f_clk / 1e9, 3),
+                  "tflops_logical": round(logical / t / 1e12, 1),
+                  "tflops_executed": round(logical / (2 if sparse else 1) / t / 1e12, 1),
+                  "frac_of_2p5pf_executed": round(logical / (2 if sparse else 1) / t / 2.5e15, 4),
+                  "cycles_per_instruction_per_simd": round(t * f_clk * n_simd / n_ins, 2)})
+    ops = {pk.HSP_VALU_EXP2: "v_exp_f32", pk.HSP_VALU_FMA: "v_fma_f32",
+           pk.HSP_VALU_MAX3: "v_max3_f32", pk.HSP_VALU_CVT: "v_cvt_pk_bf16_f32",
+           pk.HSP_VALU_SOFTMAX: "softmax_mix", pk.HSP_VALU_DOT2: "v_dot2c_f32_bf16"}
+    for op in ops:
+        for waves in (4, 8, 16):
+            for chains in (8, 16):
+                vit = 8192 * 8 // chains
+                t = timed(lambda: pk.valu_loop(op, grid, waves, vit, out, clk, chains))
+                # softmax mix: per 8 scores 8 FMA + 8 exp + 4 pack + 4 dot2 + 4 max3 = 28 ops
+                per_round = chains * 28 // 8 if op == pk.HSP_VALU_SOFTMAX else chains
+                n_ins = grid * waves * vit * per_round
+                rec = {"peak": "valu_loop", "instruction": ops[op], "chains": chains,
+                       "waves_per_simd": waves // 4, "ms": round(t * 1e3, 4),
+                       "shader_clock_ghz": round(clock_hz() / 1e9, 3),
+                       "cycles_per_wave_instruction_per_simd":
+                           round(t * clock_hz() * n_simd / n_ins, 2)}
+                if op == pk.HSP_VALU_SOFTMAX:
+                    rec["cycles_per_score_per_simd"] = round(
+                        t * clock_hz() * n_simd / (grid * waves * vit * chains * 64), 4)
+                emit(rec)
+    # Matrix core and vector ALU in one wave: 4 MFMAs (32x32x16) plus nops vector ops per round.
+    mit = 2048
+    for op in (pk.HSP_VALU_EXP2, pk.HSP_VALU_FMA):
+        for waves in (4, 8):
+            base = None
+            for nops in (0, 8, 16, 32, 64):
+                t = timed(lambda: pk.mix_wave(op, nops, grid, waves, mit, out, clk))
+                rounds = grid * waves * mit / n_simd  # wave-rounds per SIMD
+                cyc = t * clock_hz() / rounds
+                base = base or cyc
+                emit({"peak": "mix_wave", "vector_op": ops[op], "ops_per_4_mfma": nops,
+                      "waves_per_simd": waves // 4, "ms": round(t * 1e3, 4),
+                      "cycles_per_wave_round_per_simd": round(cyc, 1),
+                      "extra_cycles_per_vector_op": round((cyc - base) / max(nops, 1), 2)})
+    # Matrix waves and vector waves sharing each SIMD (one of each per SIMD).
+    sit = 4096
+    for op, vit in ((pk.HSP_VALU_EXP2, 4096), (pk.HSP_VALU_FMA, 8192), (pk.HSP_VALU_MAX3, 8192),
+                    (pk.HSP_VALU_CVT, 8192), (pk.HSP_VALU_DOT2, 8192),
+                    (pk.HSP_VALU_SOFTMAX, 2048)):
+        res = {}
+        for tag, m, e in (("mfma_only", sit, 0), ("valu_only", 0, vit), ("both", sit, vit)):
+            res[tag] = timed(lambda: pk.mix_split(op, m, e, grid, out, clk))
+        emit({"peak": "mix_split", "vector_op": ops[op], "mfma_rounds": sit, "valu_rounds": vit,
+              "ms_mfma_only": round(res["mfma_only"] * 1e3, 4),
+              "ms_valu_only": round(res["valu_only"] * 1e3, 4),
+              "ms_both": round(res["both"] * 1e3, 4),
+              "overlap": round((res["mfma_only"] + res["valu_only"] - res["both"])
+                               / min(res["mfma_only"], res["valu_only"]), 3)})
+    # Streaming HBM reads of 2 GiB.
+    nbytes = 1 << 31
+    src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
+    rout = torch.empty(4096 * 256, device=dev, dtype=torch.int32)
+    if os.environ.get("HSP_SKIP_READ"):
+        return 0
+    for mode, tag in ((0, "registers"), (1, "direct_to_lds")):
+        for g in (512, 1024, 2048, 4096):
+            t = timed(lambda: pk.read(mode, src, g, rout))
+            emit({"peak": "read", "path": tag, "workgroups": g, "bytes": nbytes,
+                  "ms": round(t * 1e3, 4), "gbs": round(nbytes / t / 1e9, 1),
+                  "frac_of_8tbs": round(nbytes / t / 8e12, 4)})
+    return 0
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
+    if args.peaks:
+        return run_peaks()
     if args.suite:
         parts = args.suite.split(",")
         bad = [x for x in parts if x not in SUITE_PARTS]

@@ -1,5 +1,6 @@
-"""Build libhierasparse.so for gfx950 in-tree: hipcc compiles each csrc/*.hip to an object under
-_build/ (in parallel) and links the shared library next to this file."""
+"""Build libhierasparse.so (the attention library) and libhspeaks.so (the measurement kernels of
+include/hs_peaks.h) for gfx950 in-tree: hipcc compiles each csrc/*.hip to an object under _build/
+(in parallel) and links the shared libraries next to this file."""
 import concurrent.futures as cf
 import os
 import shutil
@@ -14,6 +15,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhierasparse.so")
 SOURCES = ["hs_api.hip", "hs_compress.hip", "hs_decode.hip", "hs_prefill.hip",
            "hs_recompress.hip", "hs_masked.hip"]
+PEAKS_LIB = os.path.join(PKG, "libhspeaks.so")
+PEAKS_SOURCES = ["hs_peaks.hip"]
 ARCH = "gfx950"
 
 
@@ -34,7 +37,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
 # accumulators; SMFMAC's accumulator is always a VGPR tuple, so dense MFMAs there use the VGPR form
 # as well (no copies between accumulation and arch registers).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"hs_prefill.hip": _VGPR_FORM, "hs_decode.hip": _VGPR_FORM}
+EXTRA = {"hs_prefill.hip": _VGPR_FORM, "hs_decode.hip": _VGPR_FORM, "hs_peaks.hip": _VGPR_FORM}
 
 
 def _compile(src, verbose):
@@ -53,16 +56,22 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = f"{LIB}.tmp{os.getpid()}"
+def _link(objs, lib, verbose):
+    tmp = f"{lib}.tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB, verbose)
     return LIB
 
 

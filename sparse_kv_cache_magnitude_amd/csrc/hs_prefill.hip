@@ -284,20 +284,23 @@ __device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool spl
 }
 
 // P^T of the current tile for GEMM2 k-step ks (16 tokens): the accumulator registers
-// 8*(ks&1) .. +7 of half ks>>1, exponentiated and packed to bf16. The bf16 values are also summed
-// (dot product with ones) into the running denominator.
+// 8*(ks&1) .. +7 of half ks>>1, exponentiated and packed to bf16. The fp32 values are also summed
+// into the running denominator with plain adds: the packed-pair dot product (v_dot2) would do it in
+// half the instructions, but on gfx950 it waits for the matrix core to drain, so every one of them
+// stalls the other wave's MFMAs on the same SIMD.
 template <class E>
 __device__ __forceinline__ void softmax_exp(WaveState<E> &w, int ks, float c, float mc, float &lsum) {
   const f32x16 &s = w.s[ks >> 1];
   const int base = 8 * (ks & 1);
   uint32_t pk[4];
+  float p[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e], c, -mc));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e + 1], c, -mc));
-    pk[e] = pack2<E>(p0, p1);
-    lsum = add_pair_bits<E>(pk[e], lsum);
+    p[2 * e] = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e], c, -mc));
+    p[2 * e + 1] = __builtin_amdgcn_exp2f(fmaf(s[base + 2 * e + 1], c, -mc));
+    pk[e] = pack2<E>(p[2 * e], p[2 * e + 1]);
   }
+  lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   const vec8<E> nw = as8<E>(make_uint4(pk[0], pk[1], pk[2], pk[3]));
   vec16<E> &pp = w.p[ks >> 1];
   pp = (ks & 1) ? __builtin_shufflevector(half8<E>(pp, 0), nw, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
