@@ -131,9 +131,8 @@ enum {
 hs_status hs_cache_sizes(const hs_shape *shape, const hs_counts *counts, hs_cache_bytes *out);
 
 /* Workspace bytes needed by hs_compress (op = HS_OP_COMPRESS: three 8-byte loss keys per block),
-   hs_decode_attn (op = HS_OP_DECODE: one uint32 split counter per batch entry, KV head and
-   group of 16 query heads, padded to 256 bytes, then the fp32 partial outputs and log-sum-exps of
-   every split; num_splits = 0 selects the same automatic split count hs_decode_attn uses) or
+   hs_decode_attn (op = HS_OP_DECODE: the fp32 partial outputs and log-sum-exps of every split;
+   num_splits = 0 selects the same automatic split count hs_decode_attn uses) or
    hs_recompress (op = HS_OP_RECOMPRESS: dense K and V [batch][kv_heads][seq_len][head_dim] bf16,
    then the compressor's keys; the counts only need to be valid). Host call. */
 hs_status hs_workspace_size(int op, const hs_shape *shape, const hs_counts *counts,
@@ -189,10 +188,10 @@ hs_status hs_recompress(const hs_shape *shape, const hs_counts *in_counts, const
    tokens: q [batch][q_heads][head_dim] -> o [batch][q_heads][head_dim] (bf16), and if lse is not
    NULL, lse [batch][q_heads] (fp32, natural log). softmax_scale <= 0 selects 1/sqrt(head_dim).
    num_splits = 0 picks the split-KV factor automatically (1..512 otherwise). 'ws' is device
-   scratch of hs_workspace_size(HS_OP_DECODE, ..., num_splits) bytes whose counter bytes (the
-   first 256-byte-padded part) must be zero when the call runs: zero-fill a new workspace once;
-   every call leaves the counters zero again, so a workspace serves any later call, of any shape,
-   on the same stream. Two calls that run at the same time must not share a workspace. */
+   scratch of hs_workspace_size(HS_OP_DECODE, ..., num_splits) bytes, with no required contents
+   (every call writes the partials it reads); it serves any later call whose size it covers. The
+   call launches the split kernel and, with more than one split, a combine kernel, both on
+   'stream'. Two calls that run at the same time must not share a workspace. */
 hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts, const hs_cache *cache,
                          const uint16_t *q, uint16_t *o, float *lse, float softmax_scale,
                          int32_t num_splits, void *ws, size_t ws_bytes, void *stream);

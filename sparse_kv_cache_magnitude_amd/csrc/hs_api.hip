@@ -1,8 +1,8 @@
 // hs_api.hip -- the C ABI of libhierasparse.so (declared in include/hierasparse.h).
 //
-// Host side only: validates every argument before anything is enqueued, computes buffer sizes,
-// and launches the gfx950 kernels of hs_compress.hip, hs_decode.hip and hs_prefill.hip on the
-// caller's stream. The library allocates nothing; all scratch comes from the caller.
+// Host side: validates every argument before anything is enqueued, computes buffer sizes, and
+// launches the gfx950 kernels of hs_compress.hip, hs_decode.hip and hs_prefill.hip on the caller's
+// stream. The library allocates nothing; all scratch comes from the caller.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -125,16 +125,10 @@ int auto_splits(const hs::Dims &d) {
   return s;
 }
 
-// Decode workspace: the split counters (one uint32 per batch entry, KV head and group of 16 query
-// heads, padded to 256 bytes; zero between calls), then the fp32 partial outputs and log-sum-exps.
-size_t decode_counter_bytes(const hs::Dims &d) {
-  const size_t n = (size_t)d.b * d.hkv * ((d.G + 15) / 16) * sizeof(uint32_t);
-  return (n + 255) / 256 * 256;
-}
-
+// Decode workspace: the fp32 partial outputs and log-sum-exps of every split.
 size_t decode_ws_bytes(const hs::Dims &d, int splits) {
   const size_t rows = (size_t)d.b * d.hq * splits;
-  return decode_counter_bytes(d) + rows * d.D * sizeof(float) + rows * sizeof(float);
+  return rows * d.D * sizeof(float) + rows * sizeof(float);
 }
 
 size_t compress_ws_bytes(const hs::Dims &d) { return (size_t)d.b * d.hkv * d.nb * 3 * sizeof(uint64_t); }
@@ -288,32 +282,49 @@ HS_API hs_status hs_recompress(const hs_shape *shape, const hs_counts *in_counts
   return ok();
 }
 
-HS_API hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts,
-                                const hs_cache *cache, const uint16_t *q, uint16_t *o, float *lse,
-                                float softmax_scale, int32_t num_splits, void *ws,
-                                size_t ws_bytes, void *stream) {
+// Arguments of a decode call, checked; the workspace is checked by the caller.
+struct DecodeCall {
   hs::Dims d;
   hs::CacheView c;
-  hs_status st = make_dims(shape, counts, &d);
+  int splits;
+  size_t need;  // workspace bytes
+};
+static hs_status check_decode(const hs_shape *shape, const hs_counts *counts,
+                              const hs_cache *cache, const uint16_t *q, const uint16_t *o,
+                              const float *lse, int32_t num_splits, DecodeCall *dc) {
+  hs_status st = make_dims(shape, counts, &dc->d);
   if (st) return st;
-  if ((st = check_cache(cache, d, &c))) return st;
+  if ((st = check_cache(cache, dc->d, &dc->c))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse", false)))
     return st;
   if (num_splits < 0 || num_splits > 512)
     return fail(HS_ERR_SHAPE, "num_splits must be in 0..512 (got %d)", num_splits);
-  const int splits = num_splits ? num_splits : auto_splits(d);
-  const size_t need = decode_ws_bytes(d, splits);
-  if (!ws || ws_bytes < need)
-    return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
-                ws ? "" : ", NULL");
-  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
-  uint32_t *counters = (uint32_t *)ws;
-  float *part_o = (float *)((char *)ws + decode_counter_bytes(d));
-  float *part_lse = part_o + (size_t)d.b * d.hq * splits * d.D;
-  hipError_t e = hs::launch_decode(d, c, q, o, lse, scale_log2(softmax_scale, d.D), splits, part_o,
-                                   part_lse, counters, (hipStream_t)stream);
+  dc->splits = num_splits ? num_splits : auto_splits(dc->d);
+  dc->need = decode_ws_bytes(dc->d, dc->splits);
+  return HS_OK;
+}
+static hs_status run_decode(const DecodeCall &dc, const uint16_t *q, uint16_t *o, float *lse,
+                            float softmax_scale, void *ws, void *stream) {
+  float *part_o = (float *)ws;
+  float *part_lse = part_o + (size_t)dc.d.b * dc.d.hq * dc.splits * dc.d.D;
+  hipError_t e = hs::launch_decode(dc.d, dc.c, q, o, lse, scale_log2(softmax_scale, dc.d.D),
+                                   dc.splits, part_o, part_lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail(HS_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+HS_API hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts,
+                                const hs_cache *cache, const uint16_t *q, uint16_t *o, float *lse,
+                                float softmax_scale, int32_t num_splits, void *ws,
+                                size_t ws_bytes, void *stream) {
+  DecodeCall dc;
+  hs_status st = check_decode(shape, counts, cache, q, o, lse, num_splits, &dc);
+  if (st) return st;
+  if (!ws || ws_bytes < dc.need)
+    return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", dc.need, ws_bytes,
+                ws ? "" : ", NULL");
+  if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return run_decode(dc, q, o, lse, softmax_scale, ws, stream);
 }
 
 HS_API hs_status hs_prefill_attn(const hs_shape *shape, const hs_counts *counts,

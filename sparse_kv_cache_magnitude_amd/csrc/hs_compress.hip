@@ -50,19 +50,23 @@ __device__ __forceinline__ void score_group(uint32_t x0, uint32_t x1, uint32_t x
 }
 
 // Fast form of the same keys for magnitudes below 256 (bf16 magnitude bits a < 0x4380): the bf16
-// bits are the high half of the fp32 value, and adding 24 to the fp32 exponent field scales it by
-// 2^24 exactly, so the truncating conversion gives floor(|x| * 2^24) < 2^32. Zero and denormal
-// inputs become tiny normal values that truncate to 0, their floor as well. At or above 256 the
-// conversion saturates to 0xFFFFFFFF, above every in-range key (255 * 2^24 = 0xFF000000): the
-// caller detects that and redoes the block with score_group.
-// fp16: the value converted to fp32 and scaled by 2^24 is an integer, truncated exactly below
-// 256 (largest key floor(255.875 * 2^24) = 0xFFE00000) and saturated from 256 on.
+// bits are the high half of the fp32 value, and the product with 2^24 is exact (denormal inputs
+// become normal values below 1 that truncate to 0, their floor as well), so the truncating
+// conversion gives floor(|x| * 2^24) < 2^32. Before the conversion the product is clamped to
+// 4294967040 (the largest fp32 below 2^32; an infinite product, or a NaN one from a non-finite
+// pattern, gives the clamp value too), so every 15-bit pattern converts in range. Magnitudes of
+// 256 or more therefore key to 0xFFFFFF00, above every in-range key (255 * 2^24 = 0xFF000000):
+// the caller detects that and redoes the block with score_group.
+// fp16: the value converted to fp32 and scaled by 2^24 is an integer, exact below 256 (largest
+// key floor(255.875 * 2^24) = 0xFFE00000), clamped the same way from 256 on.
 template <class E>
 __device__ __forceinline__ uint32_t fixed_mag_small(uint32_t a) {
+  float v;
   if constexpr (__is_same(E, _Float16))
-    return (uint32_t)((float)__builtin_bit_cast(_Float16, (uint16_t)a) * 16777216.0f);
+    v = (float)__builtin_bit_cast(_Float16, (uint16_t)a) * 16777216.0f;
   else
-    return (uint32_t)__uint_as_float((a << 16) + (24u << 23));
+    v = __uint_as_float(a << 16) * 16777216.0f;
+  return (uint32_t)fminf(v, 4294967040.0f);
 }
 // The two dropped values of a group are its two smallest keys (the key is monotone in the
 // magnitude, and which of two equal magnitudes is dropped does not change the sum).

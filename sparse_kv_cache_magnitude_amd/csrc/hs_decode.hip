@@ -13,9 +13,10 @@
 //     S^T = K Q^T   dense block: 16 v_mfma_f32_16x16x32_bf16; 2:4 block: 8 v_smfmac_f32_16x16x64_bf16
 //     online softmax per query column (exp2 domain), P^T packed to bf16 in place
 //     O^T += V^T P^T dense block: 16 MFMA over the channel-major copy; 2:4 block: 8 SMFMAC
-//   Every split writes its normalised partial o (fp32) and log-sum-exp to the workspace; the last
-//   split of each (batch entry, KV head, column group) to finish, picked by an atomic ticket,
-//   merges the splits by their log-sum-exp and writes o (bf16) and lse.
+//   Every split writes its normalised partial o (fp32) and log-sum-exp to the workspace.
+// k_decode_combine: a second launch on the same stream; merges the splits of each (batch entry,
+//   KV head, column group) by their log-sum-exp and writes o (bf16) and lse. With one split the
+//   split kernel writes o and lse itself and nothing else is launched.
 //
 // LDS tile layout (unpadded, 32 KB per stage): K rows are stored in the MFMA row order
 // (tile_token), V^T rows in channel order. The 16-byte units of every row are XOR-swizzled by a
@@ -46,16 +47,9 @@ struct DecodeArgs {
   uint16_t *o;
   float *lse;
   float *part_o, *part_lse;
-  uint32_t *counters;
   int nb, total_w, hkv, hq, G, splits;
   float scale_log2;
 };
-
-// Device-scope (coherent across the XCDs' L2 caches) relaxed store of a float.
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Row swizzles: 128-byte rows (8 units, 16 rows per operand read) and 64-byte rows (4 units).
 __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -412,61 +406,66 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
     }
   }
 
-  // ---- normalised partial output and log-sum-exp of this split ----
+  // ---- normalised output of this split and its log-sum-exp ----
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  const size_t row0 = ((size_t)bi * a.hq + hq0) * a.splits;  // partial row of column 0, split 0
-  if (live) {
-    const size_t row = row0 + (size_t)col * a.splits + split;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float *po = a.part_o + row * kD + 4 * g;
+  if (!live) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse_s = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  if (a.splits == 1) {  // the whole head in one split: this is the output
+    const size_t orow = (size_t)bi * a.hq + hq0 + col;
+    uint16_t *op = a.o + orow * kD + 4 * g;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store_coherent(po + 16 * ct + i, oacc[ct][i] * inv);
-    if (g == 0)
-      store_coherent(a.part_lse + row, l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY);
+      *reinterpret_cast<uint2 *>(op + 16 * ct) =
+          make_uint2(pack2<E>(oacc[ct][0] * inv, oacc[ct][1] * inv),
+                     pack2<E>(oacc[ct][2] * inv, oacc[ct][3] * inv));
+    if (a.lse && g == 0) a.lse[orow] = lse_s;
+    return;
   }
+  const size_t row = ((size_t)bi * a.hq + hq0 + col) * a.splits + split;
+  float *po = a.part_o + row * kD + 4 * g;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+    *reinterpret_cast<f32x4 *>(po + 16 * ct) = oacc[ct] * inv;
+  if (g == 0) a.part_lse[row] = lse_s;
+}
 
-  // ---- log-sum-exp combine, §IV-C: the last split of this (batch entry, KV head, column group)
-  // to finish, picked by an atomic ticket, merges all splits; no workgroup waits for another.
-  // The partials were written through to the device coherence point (device-scope stores, which
-  // leave no dirty lines in the per-XCD L2) and have completed before the ticket is taken; the
-  // merging split invalidates its caches (device-scope acquire) before it reads them.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  uint32_t *ctr = a.counters + (size_t)blockIdx.z * gridDim.y + blockIdx.y;
-  uint32_t ticket = 0;
-  if (lane == 0)
-    ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  ticket = __shfl(ticket, 0, 64);
-  if (ticket != (uint32_t)(a.splits - 1)) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  combine<E>(a, row0, (size_t)bi * a.hq + hq0, ncol, lane);
+// ---- log-sum-exp combine of the splits, §IV-C: one wave per (batch entry, KV head, column group)
+// merges the partials the split kernel left in the workspace. It is a second launch on the same
+// stream, so the stream order alone makes every split's partials visible to it.
+template <class E>
+__global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
+  const int h = blockIdx.y % a.hkv, cg = blockIdx.y / a.hkv, bi = blockIdx.z;
+  const int hq0 = h * a.G + 16 * cg, ncol = min(16, a.G - 16 * cg);
+  combine<E>(a, ((size_t)bi * a.hq + hq0) * a.splits, (size_t)bi * a.hq + hq0, ncol,
+             threadIdx.x);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                          float *lse, float scale_log2, int splits, float *part_o, float *part_lse,
-                         uint32_t *counters, hipStream_t stream) {
+                         hipStream_t stream) {
   // Loads of one head's visible blocks (the per-tile counts of tile_loads, times tiles per block).
   const int total_w =
       (d.B / kTile) * (d.ndk * 16 + d.nsk * 9 + d.ndv * 16 + d.nsv * (d.B == 64 ? 9 : 12));
-  DecodeArgs a{c, q, o, lse, part_o, part_lse, counters, d.nb, total_w, d.hkv, d.hq, d.G, splits,
+  DecodeArgs a{c, q, o, lse, part_o, part_lse, d.nb, total_w, d.hkv, d.hq, d.G, splits,
                scale_log2};
   const int col_groups = (d.G + 15) / 16;
-  const dim3 grid(splits, d.hkv * col_groups, d.b);
+  const dim3 grid(splits, d.hkv * col_groups, d.b), grid_c(1, d.hkv * col_groups, d.b);
   if (d.dtype == kF16) {
     if (d.B == 64)
       k_decode_split<64, _Float16><<<grid, 64, 0, stream>>>(a);
     else
       k_decode_split<128, _Float16><<<grid, 64, 0, stream>>>(a);
+    if (splits > 1) k_decode_combine<_Float16><<<grid_c, 64, 0, stream>>>(a);
   } else {
     if (d.B == 64)
       k_decode_split<64, __bf16><<<grid, 64, 0, stream>>>(a);
     else
       k_decode_split<128, __bf16><<<grid, 64, 0, stream>>>(a);
+    if (splits > 1) k_decode_combine<__bf16><<<grid_c, 64, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -37,11 +37,11 @@ hipError_t launch_pack(const Dims &d, const uint16_t *k, const uint16_t *v, cons
 hipError_t launch_modes(const Dims &d, const uint8_t *mode_k, const uint8_t *mode_v,
                         const CacheView &c, int32_t *head_status, hipStream_t stream);
 
-// counters: one uint32 per (batch entry, KV head, column group of 16 query heads), zero before
-// the call and zero again after it.
+// part_o [b][hq][splits][D] and part_lse [b][hq][splits] fp32: the splits' partials (unused with
+// one split).
 hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                          float *lse, float scale_log2, int splits, float *part_o, float *part_lse,
-                         uint32_t *counters, hipStream_t stream);
+                         hipStream_t stream);
 
 hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                           float *lse, float scale_log2, bool smfmac, hipStream_t stream);

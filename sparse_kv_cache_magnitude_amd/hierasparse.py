@@ -206,5 +206,4 @@ def alloc_cache(shp, cnt, device="cuda"):
 
 def alloc_workspace(op, shp, cnt, num_splits=0, device="cuda"):
     n = hs_workspace_size(op, shp, cnt, num_splits)
-    # zero-filled: the decode's split counters must start at zero (each call leaves them zero)
     return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)

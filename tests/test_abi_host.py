@@ -54,9 +54,8 @@ def test_workspace_sizes():
     shp, cnt = hs.shape(2, 8, 2, 1024, 128, 64), hs.counts(1, 3, 4)
     assert hs.hs_workspace_size(hs.HS_OP_COMPRESS, shp, cnt) == 2 * 2 * 16 * 3 * 8
     for s in (1, 7, 512):
-        # 256 bytes of split counters (2 x 2 x 1 groups, padded), then the fp32 partial output
-        # (head_dim) and log-sum-exp per (batch, query head, split)
-        assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) == 256 + 2 * 8 * s * (128 + 1) * 4
+        # the fp32 partial output (head_dim) and log-sum-exp per (batch, query head, split)
+        assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) == 2 * 8 * s * (128 + 1) * 4
     assert hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, 0) > 0
     # dense K and V bf16 of the whole shape, then the compressor's keys
     assert hs.hs_workspace_size(hs.HS_OP_RECOMPRESS, shp, cnt) == \

@@ -139,26 +139,29 @@ def test_decode_deterministic():
 
 
 def test_decode_workspace_reuse():
-    """One zero-filled workspace serves calls of different shapes and split counts in a row: the
-    split counters at its start are zero again after every call, and every output is correct."""
+    """One workspace, left with whatever the previous call wrote, serves calls of different shapes
+    and split counts in a row, including a later call with more batch entries (batch 8, then
+    batch 16 at 8 KV heads) and a one-split call; every output is correct."""
     rng = np.random.default_rng(21)
     cases = [(2, 40, 2, 64 * 11, 64, (2, 5, 3), 7),    # G = 20: two column groups per KV head
              (1, 8, 2, 128 * 9, 128, (1, 4, 4), 3),
-             (2, 40, 2, 64 * 11, 64, (2, 5, 3), 0)]
+             (2, 40, 2, 64 * 11, 64, (2, 5, 3), 0),
+             (8, 32, 8, 64 * 4, 64, (1, 2, 1), 0),
+             (16, 32, 8, 64 * 4, 64, (1, 1, 2), 0),
+             (2, 8, 2, 64 * 6, 64, (1, 2, 3), 1)]       # one split: no combine launch
     shapes = [(hs.shape(b, hq, hkv, L, 128, B), hs.counts(*c), s) for b, hq, hkv, L, B, c, s in cases]
     n = max(hs.hs_workspace_size(hs.HS_OP_DECODE, shp, cnt, s) for shp, cnt, s in shapes)
-    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    groups = max(b * hkv * ((hq // hkv + 15) // 16) for b, hq, hkv, *_ in cases)
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")   # not zero: no contents needed
     for (b, hq, hkv, L, B, counts, splits), (shp, cnt, _) in zip(cases, shapes):
         K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
         V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
         q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
-        cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+        shp_d = shp
+        cache = gu.gpu_compress(shp_d, cnt, gu.to_dev(K), gu.to_dev(V))
         o = torch.empty((b, hq, 128), dtype=torch.int16, device="cuda")
         lse = torch.empty((b, hq), dtype=torch.float32, device="cuda")
         hs.hs_decode_attn(shp, cnt, cache, gu.to_dev(q), o, lse, 0.0, splits, ws)
         torch.cuda.synchronize()
-        assert (ws[:4 * groups] == 0).all(), "split counters not reset"
         ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
         assert_close(synth.bf16_to_f32(gu.to_host_u16(o)), ref, lse.cpu().numpy(), ref_lse,
                      f"reuse b={b} hq={hq} B={B} splits={splits}")

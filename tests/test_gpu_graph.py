@@ -1,7 +1,7 @@
 """The decode and prefill entry points inside a captured HIP graph (torch.cuda.CUDAGraph on ROCm):
 every replay, with eager work and synchronisations between replays, gives the eager result bit
-for bit. The library issues no memset and allocates nothing, and the decode's split counters are
-reset by the kernel itself, so a captured call can be replayed as is."""
+for bit. The library issues no memset and allocates nothing, and the decode's workspace needs no
+contents (each call writes the partials it reads), so a captured call can be replayed as is."""
 import numpy as np
 import pytest
 import torch
