@@ -196,6 +196,22 @@ hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts, const h
                          const uint16_t *q, uint16_t *o, float *lse, float softmax_scale,
                          int32_t num_splits, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the device array hs_decode_attn_noalloc uses instead of a workspace (16 MiB). */
+#define HS_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* hs_decode_attn without a workspace, for callers that cannot allocate device memory (code under
+   HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the splits' partials
+   live in a device array of HS_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on
+   each GPU until the process ends. Arguments, outputs and results are those of hs_decode_attn
+   (same kernels, same split count). A call whose hs_workspace_size(HS_OP_DECODE, ..., num_splits)
+   exceeds the array returns HS_ERR_WORKSPACE and launches nothing. The call allocates nothing
+   and launches only the decode's own kernels. Every call on a GPU shares that GPU's array: two
+   calls that overlap in time on one GPU (different streams, or different threads) race and give
+   wrong results; calls ordered on one stream are safe. */
+hs_status hs_decode_attn_noalloc(const hs_shape *shape, const hs_counts *counts,
+                                 const hs_cache *cache, const uint16_t *q, uint16_t *o, float *lse,
+                                 float softmax_scale, int32_t num_splits, void *stream);
+
 /* Causal prefill attention: q [batch][q_heads][seq_len][head_dim] -> o (same shape, bf16) and,
    if lse is not NULL, lse [batch][q_heads][seq_len]. Query position i attends the visible tokens
    t <= i of the compressed cache of the same sequence. flags: HS_PREFILL_SMFMAC or

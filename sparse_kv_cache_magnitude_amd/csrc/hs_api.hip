@@ -2,10 +2,13 @@
 //
 // Host side: validates every argument before anything is enqueued, computes buffer sizes, and
 // launches the gfx950 kernels of hs_compress.hip, hs_decode.hip and hs_prefill.hip on the caller's
-// stream. The library allocates nothing; all scratch comes from the caller.
+// stream. The library allocates nothing: scratch comes from the caller, except for
+// hs_decode_attn_noalloc, whose scratch is a fixed device array declared here.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "hierasparse.h"
 #include "hs_internal.h"
@@ -324,6 +327,55 @@ HS_API hs_status hs_decode_attn(const hs_shape *shape, const hs_counts *counts,
     return fail(HS_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", dc.need, ws_bytes,
                 ws ? "" : ", NULL");
   if (!aligned16(ws)) return fail(HS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return run_decode(dc, q, o, lse, softmax_scale, ws, stream);
+}
+
+// ---- allocation-free decode -------------------------------------------------------------------
+// The decode's workspace (the splits' partials) in a file-scope device array. Each GPU holds its
+// own copy until the process ends. In host code 'scratch' names a host-side stand-in: its device
+// address, per device, comes from hipGetSymbolAddress on the first call on that device and is
+// the only form in which the array reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[HS_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of 'scratch' on the current device (resolved once per device). Nothing in the
+// array needs to start at any value: every call writes the partials it reads.
+hs_status scratch_on_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HS_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS_OK;
+}
+}  // namespace
+
+HS_API hs_status hs_decode_attn_noalloc(const hs_shape *shape, const hs_counts *counts,
+                                        const hs_cache *cache, const uint16_t *q, uint16_t *o,
+                                        float *lse, float softmax_scale, int32_t num_splits,
+                                        void *stream) {
+  DecodeCall dc;
+  hs_status st = check_decode(shape, counts, cache, q, o, lse, num_splits, &dc);
+  if (st) return st;
+  if (dc.need > HS_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(HS_ERR_WORKSPACE,
+                "decode needs %zu bytes of scratch, more than the %zu bytes the library holds; "
+                "use hs_decode_attn with a workspace (or fewer splits)",
+                dc.need, (size_t)HS_DECODE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = scratch_on_device(&ws))) return st;
   return run_decode(dc, q, o, lse, softmax_scale, ws, stream);
 }
 

@@ -19,8 +19,11 @@ HS_BF16, HS_F16 = 0, 1
 HS_PREFILL_SMFMAC, HS_PREFILL_DECOMPRESS = 0, 1
 
 EXPORTS = ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
-           "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_prefill_attn",
-           "hs_status_string", "hs_last_error")
+           "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_decode_attn_noalloc",
+           "hs_prefill_attn", "hs_status_string", "hs_last_error")
+
+# Bytes of the device array hs_decode_attn_noalloc uses (HS_DECODE_NOALLOC_SCRATCH_BYTES).
+HS_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 CACHE_FIELDS = ("map_k", "map_v", "k_dense", "k_nnz", "k_meta", "v_dense", "v_nnz", "v_meta")
 
@@ -74,10 +77,13 @@ def lib():
                                     P, ctypes.c_size_t, P]
         L.hs_decode_attn.argtypes = [S(HsShape), S(HsCounts), S(HsCache), P, P, P, ctypes.c_float,
                                      ctypes.c_int32, P, ctypes.c_size_t, P]
+        L.hs_decode_attn_noalloc.argtypes = [S(HsShape), S(HsCounts), S(HsCache), P, P, P,
+                                             ctypes.c_float, ctypes.c_int32, P]
         L.hs_prefill_attn.argtypes = [S(HsShape), S(HsCounts), S(HsCache), P, P, P,
                                       ctypes.c_float, ctypes.c_uint32, P]
         for f in ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
-                  "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_prefill_attn"):
+                  "hs_compress_masked", "hs_recompress", "hs_decode_attn",
+                  "hs_decode_attn_noalloc", "hs_prefill_attn"):
             getattr(L, f).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -179,6 +185,14 @@ def hs_decode_attn(shp, cnt, cache, q, o, lse=None, softmax_scale=0.0, num_split
                                 float(softmax_scale), int(num_splits), _ptr(ws),
                                 ws.numel() * ws.element_size() if ws is not None else 0,
                                 _stream(stream)))
+
+
+def hs_decode_attn_noalloc(shp, cnt, cache, q, o, lse=None, softmax_scale=0.0, num_splits=0,
+                           stream=None):
+    _check(lib().hs_decode_attn_noalloc(ctypes.byref(shp), ctypes.byref(cnt),
+                                        ctypes.byref(_cache_struct(cache)), _ptr(q), _ptr(o),
+                                        _ptr(lse), float(softmax_scale), int(num_splits),
+                                        _stream(stream)))
 
 
 def hs_prefill_attn(shp, cnt, cache, q, o, lse=None, softmax_scale=0.0,

@@ -177,6 +177,26 @@ def test_workspace_checks():
         == hs.HS_ERR_SHAPE
 
 
+def test_decode_noalloc_checks():
+    """The allocation-free decode rejects, before touching the GPU, every call the plain decode
+    rejects, and every call whose workspace would not fit its fixed scratch array."""
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    call = lambda shp, cnt, c=cache, q=FAKE, splits=0: _status(lambda: _raise(
+        hs.lib().hs_decode_attn_noalloc(ctypes.byref(shp), ctypes.byref(cnt),
+                                        ctypes.byref(_cache_struct(c)), q, FAKE, None, 0.0,
+                                        splits, None)))
+    assert call(SHP, CNT, q=None) == hs.HS_ERR_NULL
+    assert call(SHP, CNT, q=MISALIGNED) == hs.HS_ERR_ALIGN
+    assert call(SHP, CNT, splits=513) == hs.HS_ERR_SHAPE
+    assert call(SHP, hs.counts(-1, 0, 0)) == hs.HS_ERR_COUNTS
+    # 64 x 32 query heads x 512 splits of 129 floats: far beyond the 16 MiB array
+    big = hs.shape(64, 32, 8, 64 * 1024, 128, 64)
+    assert hs.hs_workspace_size(hs.HS_OP_DECODE, big, hs.counts(0, 0, 0), 512) > \
+        hs.HS_DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(big, hs.counts(0, 0, 0), splits=512) == hs.HS_ERR_WORKSPACE
+    assert "scratch" in hs.hs_last_error()
+
+
 def _compress_ex(shp, cnt, pol, k, v, cache, ws, ws_bytes):
     _raise(hs.lib().hs_compress_ex(ctypes.byref(shp), ctypes.byref(cnt),
                                    ctypes.byref(pol) if pol is not None else None, k, v,
