@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-dense-baseline", action="store_true")
     p.add_argument("--cpu-sample-heads", type=int, default=16,
                    help="(batch, KV head) pairs the oracle runs for the CPU baseline")
+    p.add_argument("--cpu-leg", action="store_true",
+                   help="(internal) run one CPU-oracle leg and print its JSON line")
     p.add_argument("--copy-probe", action="store_true",
                    help="first run a plain device copy of COPY_BYTES (reads and writes a known "
                         "number of bytes: the calibration of rocprofv3's byte counters)")
@@ -197,24 +199,10 @@ def summarize_counters(fetch_dir, write_dir):
 
 def make_inputs(w, torch, dev, dtype=None):
     """Seeded N(0,1) K, V, prompt Q and decode q of the workload shape (bf16, or the torch dtype
-    given), drawn on the device (torch's seeded generator; the timing does not depend on the
-    values), with the workload's key outlier channels scaled by 8."""
-    dtype = dtype or torch.bfloat16
-    g = torch.Generator(device=dev)
-    g.manual_seed(w.seed)
-    K = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
-    K = K.to(dtype)
-    if w.outliers:
-        for h in range(w.hkv):
-            ch = torch.randperm(w.D, generator=g, device=dev)[:w.outliers]
-            K[:, h, :, ch] *= 8
-    V = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev,
-                    dtype=torch.float32).to(dtype)
-    Q = torch.empty((w.b, w.hq, w.L, w.D), device=dev, dtype=dtype)
-    for bi in range(w.b):
-        Q[bi] = torch.randn((w.hq, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
-    q = torch.randn((w.b, w.hq, w.D), generator=g, device=dev, dtype=torch.float32)
-    return K, V, Q, q.to(dtype)
+    given), drawn on the device with the workload's key outlier channels scaled by 8
+    (synth.make_inputs_device; the timing does not depend on the values)."""
+    from sparse_kv_cache_magnitude_amd import synth
+    return synth.make_inputs_device(w, dtype, dev)
 
 
 def cpu_baseline(w, heads, min_seconds=10.0):
@@ -249,6 +237,63 @@ def cpu_baseline(w, heads, min_seconds=10.0):
                       f"{w.L} tokens, repeated {reps}x; compress of the same heads took "
                       f"{t1 - t0:.2f} s",
             "decode_s_per_rep": round(per, 4), "compress_s": round(t1 - t0, 3)}
+
+
+def cpu_prefill_sample(q_heads=4, stride=64):
+    """The oracle's causal prefill on the 16K, 128-token-block workload, on a row sample: the first
+    q_heads query heads, every stride-th query row plus every row of the first and the last block.
+    The full time is extrapolated by visible (query, key) pairs (the workload prunes no block, so
+    row i sees i + 1 keys); the sampled call includes the oracle's decompression of the whole
+    cache, which the extrapolation scales with the rest (an overestimate)."""
+    import numpy as np
+    import oracle
+    from oracle import Dims
+    from sparse_kv_cache_magnitude_amd import synth
+    w = synth.workload("prefill_16k_b1_B128")
+    K, V = synth.make_kv(w.seed, w.b, w.hkv, w.L, w.D, outliers=w.outliers)
+    d = Dims(w.b, w.hkv, w.L, w.D, w.B, *w.counts())
+    cache = oracle.compress(d, K, V)
+    Q = synth.make_q(w.seed, w.b, w.hq, w.L, w.D)
+    per_head = sorted(set(range(0, w.L, stride)) | set(range(w.B)) |
+                      set(range(w.L - w.B, w.L)))
+    rows = np.array([h * w.L + r for h in range(q_heads) for r in per_head], np.int64)
+    t0 = time.perf_counter()
+    oracle.prefill(d, cache, Q, rows=rows)
+    t = time.perf_counter() - t0
+    pairs_sample = float(sum(r + 1 for r in per_head)) * q_heads
+    pairs_total = float(w.L) * (w.L + 1) / 2 * w.hq * w.b
+    return {"workload": w.name, "sample_rows": int(len(rows)), "sample_s": round(t, 3),
+            "extrapolated_ms": round(t * pairs_total / pairs_sample * 1e3, 1),
+            "method": f"{q_heads} of {w.hq} query heads, every {stride}th row and the first and "
+                      f"last {w.B}-token blocks; scaled by visible (query, key) pairs "
+                      f"({pairs_total / pairs_sample:.1f}x); extrapolated"}
+
+
+def cpu_leg(heads):
+    """One CPU-oracle leg (run in a child process, whose OMP_NUM_THREADS sets its threads): the
+    decode/compress baseline of the headline workload and the sampled 16K prefill; one JSON line."""
+    from sparse_kv_cache_magnitude_amd import synth
+    rec = cpu_baseline(synth.workload(WORKLOAD), heads)
+    rec["prefill_16k"] = cpu_prefill_sample()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def cpu_legs(heads):
+    """The oracle timed at one thread and at all the threads it may use (OMP_NUM_THREADS, else the
+    CPU count), each in a child process started before this process touches the GPU."""
+    import subprocess
+    all_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    out = {}
+    for n in sorted({1, all_threads}):
+        env = dict(os.environ, OMP_NUM_THREADS=str(n))
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg",
+                            "--cpu-sample-heads", str(heads)], env=env, capture_output=True,
+                           text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError(f"CPU oracle leg ({n} threads) failed:\n{r.stderr[-2000:]}")
+        out[n] = json.loads(r.stdout.strip().splitlines()[-1])
+    return out[all_threads], out[1]
 
 
 def run_suite(parts=SUITE_PARTS, reps=7):
@@ -614,6 +659,14 @@ def run_peaks(reps=3):
               "ms_both": round(res["both"] * 1e3, 4),
               "overlap": round((res["mfma_only"] + res["valu_only"] - res["both"])
                                / min(res["mfma_only"], res["valu_only"]), 3)})
+    # LDS read bandwidth per CU (one workgroup per CU, 4 / 8 / 16 waves).
+    for waves in (4, 8, 16):
+        lit = 4096
+        t = timed(lambda: pk.lds_read(grid, waves, lit, out, clk))
+        nbytes_l = grid * waves * lit * 8 * 1024
+        emit({"peak": "lds_read", "instruction": "ds_read_b128", "waves_per_cu": waves,
+              "ms": round(t * 1e3, 4), "shader_clock_ghz": round(clock_hz() / 1e9, 3),
+              "bytes_per_clock_per_cu": round(nbytes_l / (t * clock_hz() * 256), 1)})
     # Streaming HBM reads of 2 GiB.
     nbytes = 1 << 31
     src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
@@ -631,6 +684,8 @@ def run_peaks(reps=3):
 
 def main():
     args = parse()
+    if args.cpu_leg:
+        return cpu_leg(args.cpu_sample_heads)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
     if args.peaks:
@@ -647,6 +702,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
+
+    # The CPU-oracle legs run first, as child processes, before this process initialises the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_legs(args.cpu_sample_heads)
 
     import numpy as np
     import torch
@@ -827,8 +885,35 @@ def main():
                                        4 * w.D * w.L * (w.L + 1) / 2 * w.hq * w.b / executed, 3)}
         del cache0
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+    # Config-1 latency: one KV head, 4K tokens, every block 2:4, decode batch 1 (cache-resident,
+    # so latency only; median of 21 event windows, no settle pass).
+    w1 = synth.workload("decode_1h_4k_all24")
+    K1, V1, _, q1 = make_inputs(w1, torch, dev)
+    shp1, cnt1 = hs.shape(w1.b, w1.hq, w1.hkv, w1.L, w1.D, w1.B), hs.counts(*w1.counts())
+    cache1 = hs.alloc_cache(shp1, cnt1)
+    hs.hs_compress(shp1, cnt1, K1, V1, cache1, hs.alloc_workspace(hs.HS_OP_COMPRESS, shp1, cnt1))
+    ws1, o1 = hs.alloc_workspace(hs.HS_OP_DECODE, shp1, cnt1), torch.empty_like(q1)
+    t1 = []
+    for r in range(22):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        hs.hs_decode_attn(shp1, cnt1, cache1, q1, o1, None, 0.0, 0, ws1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            t1.append(a.elapsed_time(b) * 1e3)
+    out["config1_decode_us"] = {"workload": w1.name, "median_us": round(float(np.median(t1)), 2),
+                                "min_us": round(float(np.min(t1)), 2)}
+
+    if cpu is not None:
+        all_t, one_t = cpu
+        prefill_all = all_t.pop("prefill_16k")
+        prefill_one = one_t.pop("prefill_16k")
+        out["cpu_baseline"] = all_t
+        out["cpu_baseline_1thread"] = one_t
+        out["cpu_prefill_16k_extrapolated"] = {
+            "all_threads": {**prefill_all, "cores": all_t["cores"]},
+            "one_thread": {**prefill_one, "cores": 1}}
 
     print(json.dumps(out), flush=True)
     return 0

@@ -68,6 +68,10 @@ int hsp_mix_wave(int op, int nops, int grid, int waves, int iters, float *out, u
 int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, float *out, uint64_t *clk,
                   void *stream);
 
+/* LDS read bandwidth: 'iters' rounds of eight ds_read_b128 per wave (1 KB of consecutive bytes
+   each, conflict-free) in workgroups of 'waves' waves (1..16). */
+int hsp_lds_read(int grid, int waves, int iters, float *out, uint64_t *clk, void *stream);
+
 /* Streaming read of 'bytes' (a multiple of 16 * 64 * 8) from 'src': mode 0 = 16-byte loads into
    registers, each workgroup one contiguous chunk; mode 1 = the same chunks through direct
    global->LDS loads (global_load_lds_dwordx4), the loads the attention kernels stage tiles with.

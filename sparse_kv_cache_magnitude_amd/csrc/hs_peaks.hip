@@ -212,6 +212,33 @@ __global__ __launch_bounds__(512) void k_mix_split(float *out, int mfma_iters, i
   clock_mark(clk, 1);
 }
 
+// LDS read bandwidth: every wave streams ds_read_b128 over a 64 KB window (each wave instruction
+// reads 1 KB of consecutive bytes, conflict-free), eight reads in flight; the values are only
+// made live (an empty asm statement takes them), so no vector arithmetic shares the issue slots.
+typedef uint32_t lds_u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(1024) void k_lds_read(float *out, int iters, uint64_t *clk) {
+  __shared__ __attribute__((aligned(16))) lds_u32x4 buf[kPadFloats / 4];
+  const int t = threadIdx.x;
+  for (int i = t; i < kPadFloats / 4; i += blockDim.x) buf[i] = lds_u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  clock_mark(clk, 0);
+  // eight fixed addresses per lane, 8 KB apart (t + 512 u < 6144 entries); the lane's index
+  // passes through an empty asm statement every round, so the reads cannot be hoisted out of the
+  // loop, and the 8 KB steps fold into the instructions' offset fields
+  int idx = t;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(idx));
+    lds_u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = buf[idx + 512 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" ::"v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
+  }
+  __syncthreads();
+  out[blockIdx.x * blockDim.x + t] = 0.f;
+  clock_mark(clk, 1);
+}
+
 // Streaming reads: workgroup g reads bytes [g * chunk, (g + 1) * chunk); chunk % 32 KB == 0.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void k_read_regs(const u32x4 *src, size_t chunk16,
@@ -329,6 +356,13 @@ HSP_API int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, floa
     case HSP_VALU_DOT2: k_mix_split<HSP_VALU_DOT2><<<grid, 512, 0, s>>>(out, mfma_iters, valu_iters, c1, c2, clk); break;
     default: return -1;
   }
+  return status(hipGetLastError());
+}
+
+HSP_API int hsp_lds_read(int grid, int waves, int iters, float *out, uint64_t *clk,
+                         void *stream) {
+  if (!out || grid <= 0 || waves < 1 || waves > 16 || iters < 0) return -1;
+  k_lds_read<<<grid, 64 * waves, 0, (hipStream_t)stream>>>(out, iters, clk);
   return status(hipGetLastError());
 }
 

@@ -11,7 +11,8 @@ HSP_MFMA_32X32X16, HSP_SMFMAC_32X32X32, HSP_MFMA_16X16X32, HSP_SMFMAC_16X16X64 =
 HSP_VALU_EXP2, HSP_VALU_FMA, HSP_VALU_MAX3, HSP_VALU_CVT, HSP_VALU_SOFTMAX = 0, 1, 2, 3, 4
 HSP_VALU_DOT2 = 5
 
-EXPORTS = ("hsp_matrix_loop", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_read")
+EXPORTS = ("hsp_matrix_loop", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_lds_read",
+           "hsp_read")
 
 _lib = None
 
@@ -28,6 +29,7 @@ def lib():
         L.hsp_valu_loop.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_wave.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_split.argtypes = [I, I, I, I, P, P, P]
+        L.hsp_lds_read.argtypes = [I, I, I, P, P, P]
         L.hsp_read.argtypes = [I, P, ctypes.c_size_t, I, P, P]
         for f in EXPORTS:
             getattr(L, f).restype = I
@@ -64,6 +66,10 @@ def mix_wave(op, nops, grid, waves, iters, out, clk=None):
 def mix_split(op, mfma_iters, valu_iters, grid, out, clk=None):
     _check(lib().hsp_mix_split(op, mfma_iters, valu_iters, grid, _p(out), _p(clk), _s()),
            "mix_split")
+
+
+def lds_read(grid, waves, iters, out, clk=None):
+    _check(lib().hsp_lds_read(grid, waves, iters, _p(out), _p(clk), _s()), "lds_read")
 
 
 def read(mode, src, grid, out):

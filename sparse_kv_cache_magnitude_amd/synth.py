@@ -115,6 +115,32 @@ def random_element_mask(seed: int, X: np.ndarray, modes: np.ndarray, B: int, alo
     return out
 
 
+def make_inputs_device(w, dtype=None, dev="cuda"):
+    """The same recipe drawn on the device, for workloads too large to draw on the host in the
+    time a test or a benchmark run has: K, V [b][hkv][L][D], prompt Q [b][hq][L][D] and decode q
+    [b][hq][D] ~ N(0,1) as torch tensors of `dtype` (default bf16, rounded from fp32), from
+    torch's generator seeded with the workload seed (K, then the outlier channels, then V, Q, q),
+    with the workload's key outlier channels (per KV head, shared by every batch entry and token)
+    scaled by 8 after rounding."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    K = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
+    K = K.to(dtype)
+    if w.outliers:
+        for h in range(w.hkv):
+            ch = torch.randperm(w.D, generator=g, device=dev)[:w.outliers]
+            K[:, h, :, ch] *= 8
+    V = torch.randn((w.b, w.hkv, w.L, w.D), generator=g, device=dev,
+                    dtype=torch.float32).to(dtype)
+    Q = torch.empty((w.b, w.hq, w.L, w.D), device=dev, dtype=dtype)
+    for bi in range(w.b):
+        Q[bi] = torch.randn((w.hq, w.L, w.D), generator=g, device=dev, dtype=torch.float32)
+    q = torch.randn((w.b, w.hq, w.D), generator=g, device=dev, dtype=torch.float32)
+    return K, V, Q, q.to(dtype)
+
+
 def block_count(frac: float, nb: int) -> int:
     """Block fraction -> integer count, round half up."""
     return int(np.floor(frac * nb + 0.5))

@@ -4,6 +4,8 @@ import functools
 import numpy as np
 import torch
 
+import oracle
+
 from sparse_kv_cache_magnitude_amd import hierasparse as hs
 from sparse_kv_cache_magnitude_amd import synth
 
@@ -33,6 +35,16 @@ def gpu_compress(shp, cnt, Kd, Vd):
     hs.hs_compress(shp, cnt, Kd, Vd, cache, ws)
     torch.cuda.synchronize()
     return cache
+
+
+def compress_checked(shp, cnt, d, K, V):
+    """Compress K, V (host 16-bit patterns) on the GPU and with the oracle; the two caches must be
+    equal byte for byte. Returns (GPU cache, oracle cache): attention references are built from
+    the oracle's cache, which the GPU cache has just been shown to equal."""
+    cache = gpu_compress(shp, cnt, to_dev(K), to_dev(V))
+    want = oracle.compress(d, K, V)
+    compare_cache(cache_to_numpy(cache), want)
+    return cache, want
 
 
 def cache_to_numpy(cache):

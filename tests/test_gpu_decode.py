@@ -1,6 +1,7 @@
-"""GPU split-KV decode (hs_decode_attn) against the oracle's fp64 attention over the decompressed
-cache. Gate: max |o - o_ref| <= 1e-2 and ||o - o_ref||_2 / ||o_ref||_2 <= 5e-3 over the whole
-output tensor."""
+"""GPU split-KV decode (hs_decode_attn) against the oracle's fp64 attention over the oracle's own
+compressed cache (the GPU cache is first checked equal to it byte for byte, in the same test).
+Gate: max |o - o_ref| <= 1e-2 beyond the bf16 output rounding and ||o - o_ref||_2 / ||o_ref||_2
+<= 5e-3 over the whole output tensor."""
 import numpy as np
 import pytest
 import torch
@@ -40,24 +41,23 @@ def assert_close(o_gpu, o_ref, lse_gpu=None, lse_ref=None, tag=""):
             assert np.abs(lg[fin] - lse_ref[fin]).max() < 2e-2
 
 
-def run_decode(w_b, hq, hkv, L, B, counts, K, V, q, splits=0, scale=0.0, cache=None):
-    shp = hs.shape(w_b, hq, hkv, L, 128, B)
+def run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=0, scale=0.0, cache=None, want=None):
+    """GPU decode of q over the GPU compression of K, V, and the oracle's decode over the oracle's
+    compression of the same K, V (checked equal). Returns (o, lse, ref, ref_lse, cache, want)."""
+    shp = hs.shape(b, hq, hkv, L, 128, B)
     cnt = hs.counts(*counts)
+    d = Dims(b, hkv, L, 128, B, *counts)
     if cache is None:
-        cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+        cache, want = gu.compress_checked(shp, cnt, d, K, V)
     qd = gu.to_dev(q)
-    o = torch.empty((w_b, hq, 128), dtype=torch.int16, device="cuda")
-    lse = torch.empty((w_b, hq), dtype=torch.float32, device="cuda")
+    o = torch.empty((b, hq, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((b, hq), dtype=torch.float32, device="cuda")
     ws = hs.alloc_workspace(hs.HS_OP_DECODE, shp, cnt, splits)
     hs.hs_decode_attn(shp, cnt, cache, qd, o, lse, scale, splits, ws)
     torch.cuda.synchronize()
     of = synth.bf16_to_f32(gu.to_host_u16(o))
-    return of, lse.cpu().numpy(), cache
-
-
-def oracle_decode(w_b, hq, hkv, L, B, counts, cache_np, q, scale=0.0):
-    d = Dims(w_b, hkv, L, 128, B, *counts)
-    return oracle.decode(d, cache_np, q, hq, scale)
+    ref, ref_lse = oracle.decode(d, want, q, hq, scale)
+    return of, lse.cpu().numpy(), ref, ref_lse, cache, want
 
 
 @pytest.mark.parametrize("name", ["decode_1h_4k_all24", "decode_llama8b_32k_b8",
@@ -67,9 +67,7 @@ def test_decode_workloads(name):
     K, V = gu.workload_kv(name)
     q = synth.make_q(w.seed, w.b, w.hq, 1, w.D)
     print(f"[decode] {name}", flush=True)
-    o, lse, cache = run_decode(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, q)
-    ref, ref_lse = oracle_decode(w.b, w.hq, w.hkv, w.L, w.B, w.counts(),
-                                 gu.cache_to_numpy(cache), q)
+    o, lse, ref, ref_lse, _, _ = run_decode(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, q)
     assert_close(o, ref, lse, ref_lse, name)
 
 
@@ -81,8 +79,7 @@ def test_decode_split_invariance(splits):
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32) * 2)
-    o, lse, cache = run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=splits)
-    ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
+    o, lse, ref, ref_lse, _, _ = run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=splits)
     assert_close(o, ref, lse, ref_lse, f"splits={splits}")
 
 
@@ -96,8 +93,7 @@ def test_decode_gqa_and_block_sizes(G, B):
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
-    o, lse, cache = run_decode(b, hq, hkv, L, B, counts, K, V, q, scale=0.05)
-    ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q, 0.05)
+    o, lse, ref, ref_lse, _, _ = run_decode(b, hq, hkv, L, B, counts, K, V, q, scale=0.05)
     assert_close(o, ref, lse, ref_lse, f"G={G} B={B}")
 
 
@@ -107,10 +103,9 @@ def test_decode_all_pruned_and_single_block():
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
-    o, lse, _ = run_decode(b, hq, hkv, L, B, (4, 0, 0), K, V, q)
-    assert (o == 0).all() and np.isneginf(lse).all()
-    o, lse, cache = run_decode(b, hq, hkv, L, B, (3, 1, 0), K, V, q)   # one visible block
-    ref, ref_lse = oracle_decode(b, hq, hkv, L, B, (3, 1, 0), gu.cache_to_numpy(cache), q)
+    o, lse, ref, ref_lse, _, _ = run_decode(b, hq, hkv, L, B, (4, 0, 0), K, V, q)
+    assert (o == 0).all() and np.isneginf(lse).all() and np.isneginf(ref_lse).all()
+    o, lse, ref, ref_lse, _, _ = run_decode(b, hq, hkv, L, B, (3, 1, 0), K, V, q)  # one block
     assert_close(o, ref, lse, ref_lse, "single visible block")
 
 
@@ -121,7 +116,7 @@ def test_decode_dense_equals_library_attention():
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
-    o, _, _ = run_decode(b, hq, hkv, L, B, (0, 0, 0), K, V, q)
+    o, _, _, _, _, _ = run_decode(b, hq, hkv, L, B, (0, 0, 0), K, V, q)
     qt = torch.from_numpy(synth.bf16_to_f32(q))
     kt = torch.from_numpy(synth.bf16_to_f32(K)).repeat_interleave(hq // hkv, dim=1)
     vt = torch.from_numpy(synth.bf16_to_f32(V)).repeat_interleave(hq // hkv, dim=1)
@@ -133,8 +128,9 @@ def test_decode_deterministic():
     w = synth.workload("decode_1h_4k_all24")
     K, V = gu.workload_kv(w.name)
     q = synth.make_q(w.seed, 1, 1, 1, 128)
-    o1, l1, cache = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q)
-    o2, l2, _ = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q, cache=cache)
+    o1, l1, _, _, cache, want = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q)
+    o2, l2, _, _, _, _ = run_decode(1, 1, 1, w.L, w.B, w.counts(), K, V, q, cache=cache,
+                                    want=want)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
@@ -156,13 +152,13 @@ def test_decode_workspace_reuse():
         K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
         V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
         q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
-        shp_d = shp
-        cache = gu.gpu_compress(shp_d, cnt, gu.to_dev(K), gu.to_dev(V))
+        d = Dims(b, hkv, L, 128, B, *counts)
+        cache, want = gu.compress_checked(shp, cnt, d, K, V)
         o = torch.empty((b, hq, 128), dtype=torch.int16, device="cuda")
         lse = torch.empty((b, hq), dtype=torch.float32, device="cuda")
         hs.hs_decode_attn(shp, cnt, cache, gu.to_dev(q), o, lse, 0.0, splits, ws)
         torch.cuda.synchronize()
-        ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
+        ref, ref_lse = oracle.decode(d, want, q, hq)
         assert_close(synth.bf16_to_f32(gu.to_host_u16(o)), ref, lse.cpu().numpy(), ref_lse,
                      f"reuse b={b} hq={hq} B={B} splits={splits}")
 
@@ -183,6 +179,5 @@ def test_decode_2to4_only_cache(B, L, counts, splits):
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     q = synth.bf16_bits(rng.standard_normal((b, hq, 1, 128), dtype=np.float32))
     print(f"[decode 2:4 only] B={B} L={L} counts={counts} splits={splits}", flush=True)
-    o, lse, cache = run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=splits)
-    ref, ref_lse = oracle_decode(b, hq, hkv, L, B, counts, gu.cache_to_numpy(cache), q)
+    o, lse, ref, ref_lse, _, _ = run_decode(b, hq, hkv, L, B, counts, K, V, q, splits=splits)
     assert_close(o, ref, lse, ref_lse, f"2:4 only B={B} {counts} s={splits}")

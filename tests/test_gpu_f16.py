@@ -1,6 +1,7 @@
 """The fp16 element type (hs_shape.dtype = HS_F16) on the GPU against the oracle: compressor, re-
-compression and caller-mask compressor bit-exact; decode and causal prefill (both 2:4 paths) to
-max |o - o_ref| <= 1e-2 beyond the fp16 output rounding and relative L2 <= 5e-3."""
+compression and caller-mask compressor bit-exact; decode and causal prefill (both 2:4 paths), over
+the oracle's own compressed cache (checked equal to the GPU's first), to max |o - o_ref| <= 1e-2
+beyond the fp16 output rounding and relative L2 <= 5e-3."""
 import numpy as np
 import pytest
 import torch
@@ -40,12 +41,11 @@ def assert_close_f16(o_gpu, o_ref, lse_gpu, lse_ref, tag):
 
 
 def compress_f16(b, hq, hkv, L, B, counts, K, V):
+    """GPU and oracle compression of fp16 K, V, checked equal; returns the oracle's cache too."""
     shp = hs.shape(b, hq, hkv, L, 128, B, dtype=F16)
     cnt = hs.counts(*counts)
-    cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
-    want = oracle.compress(Dims(b, hkv, L, 128, B, *counts, dtype=1), K, V)
-    gu.compare_cache(gu.cache_to_numpy(cache), want)
-    return shp, cnt, cache
+    cache, want = gu.compress_checked(shp, cnt, Dims(b, hkv, L, 128, B, *counts, dtype=1), K, V)
+    return shp, cnt, cache, want
 
 
 @pytest.mark.parametrize("B", [64, 128])
@@ -69,14 +69,14 @@ def test_f16_compress_workload():
 
 
 def run_decode_f16(b, hq, hkv, L, B, counts, K, V, q):
-    shp, cnt, cache = compress_f16(b, hq, hkv, L, B, counts, K, V)
+    shp, cnt, cache, want = compress_f16(b, hq, hkv, L, B, counts, K, V)
     o = torch.empty((b, hq, 128), dtype=torch.int16, device="cuda")
     lse = torch.empty((b, hq), dtype=torch.float32, device="cuda")
     ws = hs.alloc_workspace(hs.HS_OP_DECODE, shp, cnt)
     hs.hs_decode_attn(shp, cnt, cache, gu.to_dev(q), o, lse, 0.0, 0, ws)
     torch.cuda.synchronize()
     d = Dims(b, hkv, L, 128, B, *counts, dtype=1)
-    ref, ref_lse = oracle.decode(d, gu.cache_to_numpy(cache), q, hq)
+    ref, ref_lse = oracle.decode(d, want, q, hq)
     return synth.f16_to_f32(gu.to_host_u16(o)), lse.cpu().numpy(), ref, ref_lse
 
 
@@ -103,13 +103,13 @@ def test_f16_decode_workload():
 
 
 def run_prefill_f16(b, hq, hkv, L, B, counts, K, V, Q, flags, rows=None):
-    shp, cnt, cache = compress_f16(b, hq, hkv, L, B, counts, K, V)
+    shp, cnt, cache, want = compress_f16(b, hq, hkv, L, B, counts, K, V)
     o = torch.empty((b, hq, L, 128), dtype=torch.int16, device="cuda")
     lse = torch.empty((b, hq, L), dtype=torch.float32, device="cuda")
     hs.hs_prefill_attn(shp, cnt, cache, gu.to_dev(Q), o, lse, 0.0, flags)
     torch.cuda.synchronize()
     d = Dims(b, hkv, L, 128, B, *counts, dtype=1)
-    ref, ref_lse = oracle.prefill(d, gu.cache_to_numpy(cache), Q, rows=rows)
+    ref, ref_lse = oracle.prefill(d, want, Q, rows=rows)
     of = synth.f16_to_f32(gu.to_host_u16(o)).reshape(-1, 128)
     lf = lse.cpu().numpy().reshape(-1)
     if rows is not None:
@@ -148,14 +148,14 @@ def test_f16_recompress_and_masked():
     K = synth.f16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.f16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     first, second = (2, 0, 6), (2, 6, 6)
-    shp, c1, cache = compress_f16(b, hkv, hkv, L, B, first, K, V)
+    shp, c1, cache, want1 = compress_f16(b, hkv, hkv, L, B, first, K, V)
     c2 = hs.counts(*second)
     out = hs.alloc_cache(shp, c2)
     ws = hs.alloc_workspace(hs.HS_OP_RECOMPRESS, shp, c2)
     hs.hs_recompress(shp, c1, cache, c2, out, ws)
     torch.cuda.synchronize()
     d1, d2 = Dims(b, hkv, L, 128, B, *first, dtype=1), Dims(b, hkv, L, 128, B, *second, dtype=1)
-    want = oracle.recompress(d1, oracle.compress(d1, K, V), d2)
+    want = oracle.recompress(d1, want1, d2)
     gu.compare_cache(gu.cache_to_numpy(out), want)
     # the caller-mask compressor on the same shape
     mk, mv = synth.random_modes(92, b, hkv, L // B, *second)

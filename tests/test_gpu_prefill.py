@@ -1,6 +1,8 @@
-"""GPU causal prefill (hs_prefill_attn) against the oracle's fp64 causal attention over the
-decompressed cache, for both ways 2:4 tiles reach the matrix cores (SMFMAC and decompress-to-LDS).
-Gate: max |o - o_ref| <= 1e-2 and relative L2 <= 5e-3 (sampled query rows at full size)."""
+"""GPU causal prefill (hs_prefill_attn) against the oracle's fp64 causal attention over the oracle's
+own compressed cache (the GPU cache is first checked equal to it byte for byte, in the same test),
+for both ways 2:4 tiles reach the matrix cores (SMFMAC and decompress-to-LDS).
+Gate: max |o - o_ref| <= 1e-2 beyond the bf16 output rounding and relative L2 <= 5e-3 (sampled
+query rows at full size)."""
 import numpy as np
 import pytest
 import torch
@@ -17,28 +19,41 @@ pytestmark = pytest.mark.gpu
 FLAGS = {"smfmac": hs.HS_PREFILL_SMFMAC, "decompress": hs.HS_PREFILL_DECOMPRESS}
 
 
-def run_prefill(b, hq, hkv, L, B, counts, K, V, Q, flags, scale=0.0, cache=None):
+def run_prefill(b, hq, hkv, L, B, counts, K, V, Q, flags, scale=0.0, cache=None, want=None,
+                rows=None):
+    """GPU causal prefill over the GPU compression of K, V and the oracle's over the oracle's
+    compression (checked equal); rows: flat indices into [b][hq][L] to compare (None = all).
+    Returns (o, lse, ref, ref_lse, cache, want) with o, lse restricted to the rows."""
     shp = hs.shape(b, hq, hkv, L, 128, B)
     cnt = hs.counts(*counts)
+    d = Dims(b, hkv, L, 128, B, *counts)
     if cache is None:
-        cache = gu.gpu_compress(shp, cnt, gu.to_dev(K), gu.to_dev(V))
+        cache, want = gu.compress_checked(shp, cnt, d, K, V)
     qd = gu.to_dev(Q)
     o = torch.empty((b, hq, L, 128), dtype=torch.int16, device="cuda")
     lse = torch.empty((b, hq, L), dtype=torch.float32, device="cuda")
     hs.hs_prefill_attn(shp, cnt, cache, qd, o, lse, scale, flags)
     torch.cuda.synchronize()
-    return synth.bf16_to_f32(gu.to_host_u16(o)), lse.cpu().numpy(), cache
+    of = synth.bf16_to_f32(gu.to_host_u16(o)).reshape(-1, 128)
+    lf = lse.cpu().numpy().reshape(-1)
+    ref, ref_lse = oracle.prefill(d, want, Q, scale, rows=rows)
+    if rows is not None:
+        of, lf = of[rows], lf[rows]
+    return of, lf, ref, ref_lse, cache, want
 
 
 def sample_rows(b, hq, L, per_head, seed):
-    """Flat row ids into [b][hq][L]: per head the first and last rows, rows around every 64-token
-    tile edge of a few tiles, plus random rows."""
+    """Flat row ids into [b][hq][L]: per head the first and last rows, the rows on both sides of
+    the 32-query wave tiles and 64-token key tiles near both ends (0/1, 31/32, 63/64/65, 95/96,
+    and their mirrors from the end), plus random rows."""
     rng = np.random.default_rng(seed)
+    edges = {0, 1, 31, 32, 33, 63, 64, 65, 95, 96, 127, 128}
+    edges |= {L - 1 - e for e in edges}
     rows = []
     for bi in range(b):
         for h in range(hq):
             base = (bi * hq + h) * L
-            pick = {0, 1, 63, 64, 65, L - 1, L - 64}
+            pick = set(edges)
             pick.update(rng.integers(0, L, per_head).tolist())
             rows += [base + r for r in sorted(pick) if 0 <= r < L]
     return np.array(rows, np.int64)
@@ -54,9 +69,8 @@ def test_prefill_small_full_compare(path, B, counts):
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
     print(f"[prefill] {path} B={B} counts={counts}", flush=True)
-    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
-    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q)
-    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} B={B} {counts}")
+    o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
+    assert_close(o, ref, lse, ref_lse, f"{path} B={B} {counts}")
 
 
 @pytest.mark.parametrize("path", ["smfmac", "decompress"])
@@ -69,10 +83,9 @@ def test_prefill_gqa_groups(path, G):
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
-    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path], scale=0.07)
-    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q,
-                                  0.07)
-    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} G={G}")
+    o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path],
+                                             scale=0.07)
+    assert_close(o, ref, lse, ref_lse, f"{path} G={G}")
 
 
 @pytest.mark.parametrize("path", ["smfmac", "decompress"])
@@ -86,10 +99,9 @@ def test_prefill_pruned_prefix_rows_are_empty(path):
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32) * scale)
     Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
     counts = (2, 1, 1)
-    o, lse, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
-    ref, ref_lse = oracle.prefill(Dims(b, hkv, L, 128, B, *counts), gu.cache_to_numpy(cache), Q)
+    o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path])
     assert np.isneginf(ref_lse).any()   # the data makes the first blocks' rows empty
-    assert_close(o.reshape(-1, 128), ref, lse.reshape(-1), ref_lse, f"{path} empty rows")
+    assert_close(o, ref, lse, ref_lse, f"{path} empty rows")
 
 
 @pytest.mark.parametrize("path", ["smfmac", "decompress"])
@@ -100,29 +112,26 @@ def test_prefill_workload_sampled(path):
     K, V = gu.workload_kv(w.name)
     Q = synth.make_q(w.seed, w.b, w.hq, w.L, w.D)
     print(f"[prefill] {w.name} {path}", flush=True)
-    o, lse, cache = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q, FLAGS[path])
     rows = sample_rows(w.b, w.hq, w.L, 6, 7)
-    ref, ref_lse = oracle.prefill(Dims(w.b, w.hkv, w.L, 128, w.B, *w.counts()),
-                                  gu.cache_to_numpy(cache), Q, rows=rows)
-    assert_close(o.reshape(-1, 128)[rows], ref, lse.reshape(-1)[rows], ref_lse,
-                 f"{w.name} {path}")
+    o, lse, ref, ref_lse, _, _ = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q,
+                                             FLAGS[path], rows=rows)
+    assert_close(o, ref, lse, ref_lse, f"{w.name} {path}")
 
 
-def test_prefill_bench_workload_sampled():
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+def test_prefill_bench_workload_sampled(path):
     """Full-size causal prefill at the benchmark's prefill shape (32K tokens, batch 8, 32/8 heads,
     64-token blocks, 77 pruned / 307 2:4 / 128 dense blocks per head, K outlier channels) on
-    sampled rows, on the SMFMAC path the benchmark times."""
+    sampled rows (the wave- and key-tile edges near both ends of every head, and two random rows
+    per head), on both 2:4 paths (the benchmark times the SMFMAC one)."""
     w = synth.workload("decode_llama8b_32k_b8")
     K, V = gu.workload_kv(w.name)
     Q = synth.make_q(w.seed + 100, w.b, w.hq, w.L, w.D)
-    print(f"[prefill] {w.name} full-size sampled", flush=True)
-    o, lse, cache = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q,
-                                hs.HS_PREFILL_SMFMAC)
+    print(f"[prefill] {w.name} full-size sampled, {path}", flush=True)
     rows = sample_rows(w.b, w.hq, w.L, 2, 8)
-    ref, ref_lse = oracle.prefill(Dims(w.b, w.hkv, w.L, 128, w.B, *w.counts()),
-                                  gu.cache_to_numpy(cache), Q, rows=rows)
-    assert_close(o.reshape(-1, 128)[rows], ref, lse.reshape(-1)[rows], ref_lse,
-                 f"{w.name} prefill")
+    o, lse, ref, ref_lse, _, _ = run_prefill(w.b, w.hq, w.hkv, w.L, w.B, w.counts(), K, V, Q,
+                                             FLAGS[path], rows=rows)
+    assert_close(o, ref, lse, ref_lse, f"{w.name} prefill {path}")
 
 
 def test_prefill_paths_agree_and_deterministic():
@@ -132,10 +141,12 @@ def test_prefill_paths_agree_and_deterministic():
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
-    o1, l1, cache = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_SMFMAC)
-    o1b, l1b, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_SMFMAC, cache=cache)
-    o2, l2, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_DECOMPRESS,
-                            cache=cache)
+    o1, l1, _, _, cache, want = run_prefill(b, hq, hkv, L, B, counts, K, V, Q,
+                                            hs.HS_PREFILL_SMFMAC)
+    o1b, l1b, _, _, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_SMFMAC,
+                                       cache=cache, want=want)
+    o2, l2, _, _, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, hs.HS_PREFILL_DECOMPRESS,
+                                     cache=cache, want=want)
     assert np.array_equal(o1, o1b) and np.array_equal(l1, l1b)
     # the two paths multiply the same bf16 values; only accumulation order may differ
     assert np.abs(o1 - o2).max() <= 1e-2
@@ -147,9 +158,9 @@ def test_prefill_dense_equals_library_attention():
     K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
     Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
-    o, _, _ = run_prefill(b, hq, hkv, L, B, (0, 0, 0), K, V, Q, hs.HS_PREFILL_SMFMAC)
+    o, _, _, _, _, _ = run_prefill(b, hq, hkv, L, B, (0, 0, 0), K, V, Q, hs.HS_PREFILL_SMFMAC)
     qt = torch.from_numpy(synth.bf16_to_f32(Q))
     kt = torch.from_numpy(synth.bf16_to_f32(K)).repeat_interleave(hq // hkv, dim=1)
     vt = torch.from_numpy(synth.bf16_to_f32(V)).repeat_interleave(hq // hkv, dim=1)
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).numpy()
-    assert_close(o, ref.astype(np.float64), tag="prefill dense vs sdpa fp32")
+    assert_close(o, ref.astype(np.float64).reshape(-1, 128), tag="prefill dense vs sdpa fp32")
