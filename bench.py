@@ -611,6 +611,18 @@ def run_peaks(reps=3):
                   "tflops_executed": round(logical / (2 if sparse else 1) / t / 1e12, 1),
                   "frac_of_2p5pf_executed": round(logical / (2 if sparse else 1) / t / 2.5e15, 4),
                   "cycles_per_instruction_per_simd": round(t * f_clk * n_simd / n_ins, 2)})
+    # Dependent chains: each instruction accumulates into the previous one's (or the one before's)
+    # result, as a GEMM's k-steps into one output tile do.
+    for kind in (pk.HSP_MFMA_32X32X16, pk.HSP_SMFMAC_32X32X32):
+        for accs in (1, 2):
+            for waves in (4, 8):
+                t = timed(lambda: pk.matrix_chain(kind, accs, grid, waves, iters, out, clk))
+                f_clk = clock_hz()
+                n_ins = grid * waves * iters * 4
+                emit({"peak": "matrix_chain", "instruction": names[kind], "accumulators": accs,
+                      "waves_per_simd": waves // 4, "ms": round(t * 1e3, 4),
+                      "shader_clock_ghz": round(f_clk / 1e9, 3),
+                      "cycles_per_instruction_per_simd": round(t * f_clk * n_simd / n_ins, 2)})
     ops = {pk.HSP_VALU_EXP2: "v_exp_f32", pk.HSP_VALU_FMA: "v_fma_f32",
            pk.HSP_VALU_MAX3: "v_max3_f32", pk.HSP_VALU_CVT: "v_cvt_pk_bf16_f32",
            pk.HSP_VALU_SOFTMAX: "softmax_mix", pk.HSP_VALU_DOT2: "v_dot2c_f32_bf16"}

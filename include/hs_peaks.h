@@ -51,6 +51,12 @@ enum {
 int hsp_matrix_loop(int kind, int grid, int waves, int iters, float *out, uint64_t *clk,
                     void *stream);
 
+/* hsp_matrix_loop with the four instructions of a round spread round-robin over 'accumulators'
+   (1 or 2) accumulators, so that each accumulates into the result of the one 1 or 2 instructions
+   before it (a dependent chain); 'kind' HSP_MFMA_32X32X16 or HSP_SMFMAC_32X32X32. */
+int hsp_matrix_chain(int kind, int accumulators, int grid, int waves, int iters, float *out,
+                     uint64_t *clk, void *stream);
+
 /* 'iters' rounds of 'chains' (8 or 16) independent operations 'op' per wave (HSP_VALU_SOFTMAX:
    'chains' scores per round). */
 int hsp_valu_loop(int op, int chains, int grid, int waves, int iters, float *out, uint64_t *clk,

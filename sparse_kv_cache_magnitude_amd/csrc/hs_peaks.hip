@@ -54,18 +54,21 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-template <int KIND>
+// NACC accumulators per wave, used round-robin: with one, every instruction accumulates into the
+// result of the one before it (a dependent chain).
+template <int KIND, int NACC = 4>
 __device__ __forceinline__ float matrix_rounds(int iters, int tid) {
   const uint4 a = seed4(tid, 1), b0 = seed4(tid, 2), b1 = seed4(tid, 3);
   const uint32_t idx = 0x44444444u;  // 2:4 positions 0 and 1 of every group
   float s = 0.f;
   if constexpr (KIND == HSP_MFMA_32X32X16 || KIND == HSP_SMFMAC_32X32X32) {
-    f32x16 acc[4];
+    f32x16 acc[NACC];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = zero16();
+    for (int j = 0; j < NACC; ++j) acc[j] = zero16();
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int k = 0; k < 4; ++k) {
+        const int j = k % NACC;
         if constexpr (KIND == HSP_MFMA_32X32X16)
           acc[j] = hs::mma32x16(hs::as8<__bf16>(a), hs::as8<__bf16>(b0), acc[j]);
         else
@@ -74,7 +77,7 @@ __device__ __forceinline__ float matrix_rounds(int iters, int tid) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NACC; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s += acc[j][e];
   } else {
@@ -98,12 +101,12 @@ __device__ __forceinline__ float matrix_rounds(int iters, int tid) {
   return s;
 }
 
-template <int KIND>
+template <int KIND, int NACC = 4>
 __global__ __launch_bounds__(1024) void k_matrix_loop(float *out, int iters, uint64_t *clk) {
   __shared__ float pad[kPadFloats];
   clock_mark(clk, 0);
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
-  out[tid] = through_lds(pad, matrix_rounds<KIND>(iters, threadIdx.x));
+  out[tid] = through_lds(pad, matrix_rounds<KIND, NACC>(iters, threadIdx.x));
   clock_mark(clk, 1);
 }
 
@@ -289,6 +292,25 @@ HSP_API int hsp_matrix_loop(int kind, int grid, int waves, int iters, float *out
     case HSP_MFMA_16X16X32: k_matrix_loop<HSP_MFMA_16X16X32><<<g, b, 0, s>>>(out, iters, clk); break;
     case HSP_SMFMAC_16X16X64: k_matrix_loop<HSP_SMFMAC_16X16X64><<<g, b, 0, s>>>(out, iters, clk); break;
     default: return -1;
+  }
+  return status(hipGetLastError());
+}
+
+HSP_API int hsp_matrix_chain(int kind, int accumulators, int grid, int waves, int iters,
+                             float *out, uint64_t *clk, void *stream) {
+  if (!out || grid <= 0 || waves < 1 || waves > 16 || iters < 0) return -1;
+  const dim3 g(grid), b(64 * waves);
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == HSP_MFMA_32X32X16) {
+    if (accumulators == 1) k_matrix_loop<HSP_MFMA_32X32X16, 1><<<g, b, 0, s>>>(out, iters, clk);
+    else if (accumulators == 2) k_matrix_loop<HSP_MFMA_32X32X16, 2><<<g, b, 0, s>>>(out, iters, clk);
+    else return -1;
+  } else if (kind == HSP_SMFMAC_32X32X32) {
+    if (accumulators == 1) k_matrix_loop<HSP_SMFMAC_32X32X32, 1><<<g, b, 0, s>>>(out, iters, clk);
+    else if (accumulators == 2) k_matrix_loop<HSP_SMFMAC_32X32X32, 2><<<g, b, 0, s>>>(out, iters, clk);
+    else return -1;
+  } else {
+    return -1;
   }
   return status(hipGetLastError());
 }

@@ -5,26 +5,35 @@
 // §IV-C1 asynchronous K/V staging, §IV-C2 in-fragment re-layout, §IV-C3 dense and sparse buffers
 // aliased in on-chip memory. Made causal; pruned blocks are skipped without any load.
 //
-// Work decomposition: one workgroup = 8 waves (two per SIMD, one workgroup per CU). Each wave
-// owns one (query head, 32-query tile) task; a workgroup's eight tasks share one KV head (for GQA
-// group size 4: the four query heads of that KV head at two adjacent 32-query tiles), so every K/V
-// tile the workgroup stages serves 256 queries. Query tiles are issued longest-first and the
-// workgroups of one KV head run on one XCD. Two waves per SIMD cover each other's LDS, barrier
-// and transcendental latencies (the matrix cores and the VALU barely run concurrently on gfx950,
-// so a tile costs about its matrix-core time plus its softmax VALU time).
+// Work decomposition: each wave owns one (query head, 32-query tile) task; a workgroup's tasks
+// share one KV head (for GQA group size 4: the four query heads of that KV head at adjacent
+// 32-query tiles), so every K/V tile it stages serves 32 queries per wave. Query tiles are issued
+// longest-first and the workgroups of one KV head run on one XCD.
+//   SMFMAC path (heads of at most 2048 blocks): workgroups of 4 waves (one per SIMD), two
+//   workgroups per CU. The two waves on a SIMD then belong to different workgroups whose
+//   per-tile barriers are independent, so one wave's staging, barrier and dependency waits
+//   overlap the other's matrix and vector work; measured faster than 8-wave workgroups whose two
+//   waves per SIMD walk in lockstep.
+//   Decompress path (and SMFMAC for longer heads): workgroups of 8 waves (two per SIMD), one per
+//   CU.
 //
-// Per visible 64-token KV tile n (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 and
+// Per visible 64-token KV tile (matrix-core shapes 32x32: v_mfma_f32_32x32x16_bf16 and
 // v_smfmac_f32_32x32x32_bf16; all accumulators in VGPRs):
-//   staging   three LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) one
-//             tile ahead; one wait for the wave's loads and one barrier per tile. A stage holds
-//             the tile's K and V^T in their stored representation (dense copy, or kept values +
-//             metadata), rows unit-swizzled so that the operand reads are free of bank
-//             conflicts (layout below). The walk reads its tiles from a list of the
-//             workgroup's visible blocks built at start, so pruned blocks cost nothing.
+//   staging   LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4) one tile
+//             ahead; one wait for the wave's loads and one barrier per tile. A stage holds the
+//             tile's K and V^T in their stored representation (dense copy, or kept values +
+//             metadata), rows unit-swizzled so that the operand reads are free of bank conflicts
+//             (layout below). The walk reads its tiles from a list of the workgroup's visible
+//             blocks built at start, so pruned blocks cost nothing.
 //   GEMM1     S^T[64 tok][32 q] = K Q^T (Q stays in registers as the B operand).
 //   softmax   causal mask, column-wise running max (exp2 domain, lazy rescale) and
 //             P^T = exp2(S^T - max) packed to bf16 in registers.
-//   GEMM2     O^T[128 ch][32 q] += V^T P^T, for tile n-1, interleaved with the softmax of tile n.
+//   GEMM2     O^T[128 ch][32 q] += V^T P^T: in the same step (4-wave workgroups, two stages), or
+//             one tile late beside the exponentials of the next tile (8-wave workgroups, three
+//             stages).
+// When every visible block of a workgroup has both operands 2:4 (or both dense), the walk runs a
+// copy of the tile body compiled for that kind, with no per-tile branches on the operand kinds
+// (the specialised fully-2:4 and fully-dense kernels of §IV-C3).
 // Token order: GEMM1's A operand rows are the tile's tokens in an order tau chosen so that the
 // 32x32 accumulator lands exactly in GEMM2's B operand layout (lane half h holds 16 consecutive
 // registers per 32-token half); P^T needs no data movement between lanes. The stage stores the K
@@ -33,9 +42,11 @@
 // halves (so the output accumulators see one instruction type). Decompress path: after a tile has
 // landed, the whole workgroup expands its 2:4 operands once into a dense scratch tile in LDS (the
 // dense stage layout; one more barrier), and GEMM1, the softmax and GEMM2 of that tile then run on
-// dense MFMA without the one-tile GEMM2 lag.
+// dense MFMA in the same step.
 #include "hs_device.h"
 #include "hs_internal.h"
+
+#include <type_traits>
 
 namespace hs {
 namespace {
@@ -43,8 +54,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kTile = 64;   // KV tokens per tile
 constexpr int kQTile = 32;  // queries per wave
-constexpr int kWaves = 8;
-constexpr int kStages = 3;
+constexpr int kWaves = 8;  // decompress path (and the SMFMAC path for heads of > 2048 blocks)
 
 // ---- LDS stage layout (bytes). A stage holds one tile in two 16 KB regions:
 //   K region   dense: 64 rows x 256 B; 2:4: 64 rows x 128 B of kept values and the 2:4 K
@@ -61,26 +71,38 @@ constexpr int kStageBytes = 2 * kRegion;  // 32 KB
 constexpr int kMetaOff = 8192;            // K region: 2:4 K metadata
 constexpr int kCtStride = 4096;           // V^T region: bytes between 32-channel tiles
 constexpr int kVMetaOff = kRegion + 2048;  // stage: 2:4 V metadata
-// The workgroup's visible blocks in order: their modes as local pool slots (int32: K slot code in
-// the high half, V slot code in the low half; +(i+1) dense slot i, -(i+1) 2:4 slot i) and their
-// block indices (int16), plus the per-wave counts used while building the list.
-constexpr int kListModesOff = kStages * kStageBytes;
-constexpr int kListBlkOff = kListModesOff + 4 * kMaxBlocks;
-constexpr int kCountOff = kListBlkOff + 2 * kMaxBlocks;
-// SMFMAC path: 1 KB of the index word a dense V^T tile's first SMFMAC uses (0x4444, positions 0
-// and 1 of every group), laid out like a stage's V^T metadata, so dense and 2:4 tiles read their
-// index words the same way.
-constexpr int kDenseIdxOff = (kCountOff + 4 * kWaves + 15) / 16 * 16;
-// SMFMAC path: 128 zero bytes. An SMFMAC accumulates in place, so the S^T accumulators of a 2:4 K
-// tile start from zeros read here (LDS broadcast reads) rather than from 16 VALU moves per half.
-constexpr int kZeroOff = kDenseIdxOff + 1024;
-constexpr int kLdsBytes = kZeroOff + 128;  // 121 KB
-// Decompress path: the dense image of the current tile's 2:4 operands (the stage layout, K at 0,
-// V^T at kRegion), expanded once per tile by the whole workgroup.
-constexpr int kScratchOff = (kLdsBytes + 1023) / 1024 * 1024;
-constexpr int kLdsDecomp = kScratchOff + kStageBytes;  // 153 KB
-static_assert(kRegion / 1024 == 2 * kWaves && kMetaOff / 1024 == kWaves, "loads per wave");
-static_assert(kLdsBytes <= 160 * 1024 && kLdsDecomp <= 160 * 1024, "LDS budget");
+// LDS of a workgroup of W waves, stages first (each 32 KB, 1 KB aligned):
+//   stages     kStagesN tiles (SMFMAC path with W = 8: three, GEMM2 of a tile runs one tile late;
+//              W = 4: two; decompress path: three)
+//   kDenseIdx  SMFMAC path: 1 KB of the index word a dense V^T tile's first SMFMAC uses (0x4444,
+//              positions 0 and 1 of every group), laid out like a stage's V^T metadata, so dense
+//              and 2:4 tiles read their index words the same way
+//   kZero      SMFMAC path: 128 zero bytes. An SMFMAC accumulates in place, so the S^T
+//              accumulators of a 2:4 K tile start from zeros read here (LDS broadcast reads)
+//              rather than from 16 VALU moves per half
+//   kCount     per-wave counts used while building the block list; kKind per-wave operand kinds
+//              (bit 0: a visible block has a dense operand, bit 1: a 2:4 one)
+//   kListModes the workgroup's visible blocks in order: their modes as local pool slots (int32: K
+//              slot code in the high half, V slot code in the low half; +(i+1) dense slot i,
+//              -(i+1) 2:4 slot i); kListBlk their block indices (int16); kMaxB entries each
+//   kScratch   decompress path: the dense image of the current tile's 2:4 operands (the stage
+//              layout, K at 0, V^T at kRegion), expanded once per tile by the whole workgroup
+template <int W, bool kSmfmac>
+struct Lay {
+  static constexpr int kStagesN = (kSmfmac && W == 4) ? 2 : 3;
+  static constexpr int kMaxB = W == 4 ? 2048 : kMaxBlocks;
+  static constexpr int kDenseIdx = kStagesN * kStageBytes;
+  static constexpr int kZero = kDenseIdx + 1024;
+  static constexpr int kCount = kZero + 128;
+  static constexpr int kKind = kCount + 4 * W;
+  static constexpr int kListModes = (kKind + 4 * W + 15) / 16 * 16;
+  static constexpr int kListBlk = kListModes + 4 * kMaxB;
+  static constexpr int kEnd = kListBlk + 2 * kMaxB;
+  static constexpr int kScratch = (kEnd + 1023) / 1024 * 1024;
+  static constexpr int kBytes = kSmfmac ? kEnd : kScratch + kStageBytes;
+  static_assert(kBytes <= (W == 4 ? 80 : 160) * 1024, "LDS budget");
+};
+static_assert(kRegion % 1024 == 0 && kMetaOff % 1024 == 0, "whole 1 KB loads per region");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -179,10 +201,10 @@ struct LaneOffsets {
 // the metadata is needed.
 template <bool kSparseK, class E>
 __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf,
-                                      const char *lds) {
+                                      const char *zp) {
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    f32x16 acc = kSparseK ? *reinterpret_cast<const f32x16 *>(lds + kZeroOff + 64 * T) : zero16();
+    f32x16 acc = kSparseK ? *reinterpret_cast<const f32x16 *>(zp + 64 * T) : zero16();
     if (!kSparseK) {
       uint4 k[8];  // all reads issued before the first MFMA that needs them
 #pragma unroll
@@ -232,10 +254,10 @@ __device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *s
     if (!sparse) w.o[ct] = smfmac32(as8<E>(v1[ct]), w.p[u], 0xEEEEu, w.o[ct]);
   }
 }
-// Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (kDenseIdxOff).
+// Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (table at didx).
 __device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
-                                           const LaneOffsets &lo, const char *lds) {
-  const char *base = sparse ? st : lds + kDenseIdxOff - kVMetaOff;
+                                           const LaneOffsets &lo, const char *didx) {
+  const char *base = sparse ? st : didx - kVMetaOff;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) meta[ct] = lds8(base + lo.vm + ct * 32 * 8);
 }
@@ -327,11 +349,11 @@ __device__ __forceinline__ void softmax_finish(WaveState<E> &w, bool need, float
 template <class E>
 __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_prev, bool gemm,
                                                bool sparse, const LaneOffsets &lo, int hf,
-                                               float c, const char *lds) {
+                                               float c, const char *didx) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
   uint2 meta[4];
-  load_vmeta(meta, st_prev, gemm && sparse, lo, lds);
+  load_vmeta(meta, st_prev, gemm && sparse, lo, didx);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (gemm) gemm2_smfmac_step(w, st_prev, sparse, meta, u, lo, hf);
@@ -339,6 +361,16 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
     softmax_exp(w, 2 * u + 1, c, mc, lsum);
   }
   return lsum;
+}
+
+// GEMM2 of one staged tile alone.
+template <class E>
+__device__ __forceinline__ void gemm2_smfmac(WaveState<E> &w, const char *st, bool sparse,
+                                             const LaneOffsets &lo, int hf, const char *didx) {
+  uint2 meta[4];
+  load_vmeta(meta, st, sparse, lo, didx);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
 }
 
 // ---- decompress path: 2:4 operands of a stage expanded into the dense stage layout -------------
@@ -379,12 +411,15 @@ __device__ __forceinline__ void expand_tile(const char *st, char *dst, bool spar
 // by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves 3-6
 // (block 128, where a tile is half of each channel's metadata row).
 
-template <int B, bool kSmfmac, class E>
-__global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kSmfmac ? kLdsBytes : kLdsDecomp];
+template <int B, int W, bool kSmfmac, class E>
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs a) {
+  using L = Lay<W, kSmfmac>;
+  static_assert(kSmfmac || W == kWaves, "the decompress path runs eight waves");
+  __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int TPB = B / kTile;  // 64-token tiles per block
+  constexpr int kVmWave0 = W == 8 ? 3 : 0;  // block 128: first of the four V metadata waves
 
   // XCD-aware order: consecutive dispatch slots go round-robin over the 8 XCDs, so logical
   // workgroup index i*(N/8)+x runs on XCD x and one KV head's workgroups share an L2.
@@ -395,25 +430,27 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
 
   // Tasks (query head in group fastest, 32-query tiles last-first); this wave's task and the
   // workgroup's last key tile.
-  const int task = wgi * kWaves + wave;
+  const int task = wgi * W + wave;
   const bool has_task = task < a.G * a.nqt;
   const int hq_i = h * a.G + (has_task ? task % a.G : 0);
   const int qt = has_task ? a.nqt - 1 - task / a.G : 0;
-  const int qt_max = a.nqt - 1 - (wgi * kWaves) / a.G;
+  const int qt_max = a.nqt - 1 - (wgi * W) / a.G;
   const int kt_max = (kQTile * qt_max + kQTile - 1) / kTile;
   const int nbq = kt_max / TPB + 1;  // blocks touched by this workgroup
 
   // The visible blocks of this head up to the workgroup's last key tile, compacted in order
   // (ballot per wave, then the counts of the lower waves as the offset).
-  int32_t *lmodes = reinterpret_cast<int32_t *>(lds + kListModesOff);
-  int16_t *lblk = reinterpret_cast<int16_t *>(lds + kListBlkOff);
-  int32_t *wcount = reinterpret_cast<int32_t *>(lds + kCountOff);
-  if (kSmfmac && tid < 256) reinterpret_cast<uint32_t *>(lds + kDenseIdxOff)[tid] = 0x44444444u;
-  if (kSmfmac && tid < 32) reinterpret_cast<uint32_t *>(lds + kZeroOff)[tid] = 0u;
-  int n_vis = 0;
+  int32_t *lmodes = reinterpret_cast<int32_t *>(lds + L::kListModes);
+  int16_t *lblk = reinterpret_cast<int16_t *>(lds + L::kListBlk);
+  int32_t *wcount = reinterpret_cast<int32_t *>(lds + L::kCount);
+  const char *didx = lds + L::kDenseIdx, *zp = lds + L::kZero;
+  if (kSmfmac && tid < 256) reinterpret_cast<uint32_t *>(lds + L::kDenseIdx)[tid] = 0x44444444u;
+  if (kSmfmac && tid < 32) reinterpret_cast<uint32_t *>(lds + L::kZero)[tid] = 0u;
+  int32_t *wkind = reinterpret_cast<int32_t *>(lds + L::kKind);
+  int n_vis = 0, kinds = 0;
   {
     const int32_t *mkh = a.c.map_k + (size_t)head * a.nb, *mvh = a.c.map_v + (size_t)head * a.nb;
-    for (int base = 0; base < nbq; base += kWaves * 64) {
+    for (int base = 0; base < nbq; base += W * 64) {
       const int j = base + tid;
       const int mk = j < nbq ? mkh[j] : 0, mv = j < nbq ? mvh[j] : 0;
       const uint64_t vis = __builtin_amdgcn_ballot_w64(mk != 0);
@@ -423,11 +460,14 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
       __syncthreads();
       int off = n_vis;
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) {
+      for (int w2 = 0; w2 < W; ++w2) {
         const int cw = wcount[w2];
         off += w2 < wave ? cw : 0;
         n_vis += cw;
       }
+      kinds |= (__builtin_amdgcn_ballot_w64(mk != 0 && (mk > 0 || mv > 0)) != 0 ? 1 : 0) |
+               (__builtin_amdgcn_ballot_w64(mk != 0 && (mk < 0 || mv < 0)) != 0 ? 2 : 0);
+      if (lane == 0) wkind[wave] = kinds;
       if (mk != 0) {
         const int sk = mk > 0 ? mk - head * a.ndk : mk + head * a.nsk;
         const int sv = mv > 0 ? mv - head * a.ndv : mv + head * a.nsv;
@@ -438,6 +478,10 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     }
   }
   n_vis = __builtin_amdgcn_readfirstlane(n_vis);
+  kinds = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < W; ++w2) kinds |= wkind[w2];
+  kinds = __builtin_amdgcn_readfirstlane(kinds);
 
   WaveState<E> w;
   {
@@ -485,8 +529,10 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
                  : n_vis * TPB - ((__builtin_amdgcn_readfirstlane((int)lblk[n_vis - 1]) + 1) *
                                           TPB - 1 > kt_max ? 1 : 0);
   // Per-lane global byte offsets of this wave's direct loads: one per region (for K, one per
-  // GEMM1 row order, see tau). Load i of a dense region (LDS units 64 (wave + 8 i) + lane) is the
-  // same lane pattern 32 (K) or 64 (V^T) rows further on, a per-load constant.
+  // GEMM1 row order, see tau). Load i of a region (LDS bytes 1024 (wave + W i) on) is the same
+  // lane pattern 4 W i (dense K), 8 W i (2:4 K, dense V^T) or 16 W i (2:4 V^T) rows further on,
+  // a per-load constant: those row steps are multiples of 16, which the unit swizzles and the
+  // token order tau leave alone.
   uint32_t oKd[2], oKn[2], oKm[2], oVd, oVn, oVm;
   {
 #pragma unroll
@@ -502,12 +548,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     oVd = rd * (2 * B) + 16 * (cd ^ ((rd >> 1) & 7));
     const int rn = 16 * wave + (lane >> 2), cn = lane & 3;     // 2:4 V^T: 4 units per row
     oVn = rn * B + 16 * (cn ^ ((rn >> 2) & 3));
-    const int d = 64 * ((wave + 5) & 3) + lane;  // block 128: waves 3..6 -> dword loads 0..3
+    const int d = 64 * (wave - kVmWave0) + lane;  // block 128: dword loads 0..3
     oVm = B == 64 ? 16 * lane : (d >> 1) * (B / 8) + 4 * (d & 1);
   }
 
-  // Direct loads of one tile (block modes mk, mv) into a stage: dense regions two 1 KB loads per
-  // wave, 2:4 values one, metadata one load by one wave (block 128: four dword loads).
+  // Direct loads of one tile (block modes mk, mv) into a stage: dense regions 16 / W 1 KB loads
+  // per wave, 2:4 values 8 / W, metadata one load by one wave (block 128: four dword loads by
+  // waves kVmWave0 .. kVmWave0 + 3).
   const uint16_t *kd_h = a.c.k_dense + (size_t)head * a.ndk * B * kD;
   const uint16_t *kn_h = a.c.k_nnz + (size_t)head * a.nsk * B * (kD / 2);
   const uint16_t *km_h = a.c.k_meta + (size_t)head * a.nsk * B * (kD / 16);
@@ -521,33 +568,41 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
     if (mk > 0) {
       const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
       const uint32_t o = sp ? oKd[1] : oKd[0];
-      dma16(g, o, kl + 1024 * wave);
-      dma16(g + 32 * 2 * kD, o, kl + 1024 * (wave + kWaves));
+#pragma unroll
+      for (int i = 0; i < 16 / W; ++i) dma16(g + i * (4 * W) * 2 * kD, o, kl + 1024 * (wave + W * i));
     } else {
       const int row0 = (-mk - 1) * B + kTile * half;
-      dma16(uniform_ptr(kn_h + row0 * (kD / 2)), sp ? oKn[1] : oKn[0], kl + 1024 * wave);
+      const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
+      const uint32_t o = sp ? oKn[1] : oKn[0];
+#pragma unroll
+      for (int i = 0; i < 8 / W; ++i) dma16(g + i * (8 * W) * kD, o, kl + 1024 * (wave + W * i));
       if (wave == 1)
         dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
-      dma16(g, oVd, vl + 1024 * wave);
-      dma16(g + 64 * 2 * B, oVd, vl + 1024 * (wave + kWaves));
+#pragma unroll
+      for (int i = 0; i < 16 / W; ++i) dma16(g + i * (8 * W) * 2 * B, oVd, vl + 1024 * (wave + W * i));
     } else {
       const int blk = (-mv - 1) * B * kD;
+      const char *g = uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half);
       // 16 rows per load; rows 32 ct + .. start at ct * kCtStride.
-      dma16(uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half), oVn,
-            vl + (wave >> 1) * kCtStride + 1024 * (wave & 1));
+#pragma unroll
+      for (int i = 0; i < 8 / W; ++i) {
+        const int q = wave + W * i;
+        dma16(g + i * (16 * W) * B, oVn, vl + (q >> 1) * kCtStride + 1024 * (q & 1));
+      }
       const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
       if (B == 64) {
         if (wave == 2) dma16(gm, oVm, kl + kVMetaOff);
-      } else if (wave >= 3 && wave <= 6) {
-        dma4(gm, oVm, kl + kVMetaOff + 256 * (wave - 3));
+      } else if (wave >= kVmWave0 && wave < kVmWave0 + 4) {
+        dma4(gm, oVm, kl + kVMetaOff + 256 * (wave - kVmWave0));
       }
     }
   };
   const float c = a.scale_log2;
-  // Tile it of the walk is computed from stage it % 3 while tile it + 1 lands in the next stage.
+  constexpr int NS = L::kStagesN;
+  // Tile it of the walk is computed from stage it % NS while tile it + 1 lands in the next stage.
   int kt0 = 0, mk0 = 0, mv0 = 0;
   if (n_tiles > 0) {
     tile_info(0, kt0, mk0, mv0);
@@ -559,13 +614,13 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   if constexpr (!kSmfmac) {
     // Decompress path: each tile's 2:4 operands are expanded once into the dense scratch tile
     // (one more barrier), then GEMM1, the softmax and GEMM2 of the tile run on dense operands.
-    char *scratch = lds + kScratchOff;
+    char *scratch = lds + L::kScratch;
     int stage = 0;
     for (int it = 0; it < n_tiles; ++it) {
       int kt1 = 0, mk1 = 0, mv1 = 0;
       const bool more = it + 1 < n_tiles;
       if (more) tile_info(it + 1, kt1, mk1, mv1);
-      const int next_stage = stage == kStages - 1 ? 0 : stage + 1;
+      const int next_stage = stage == NS - 1 ? 0 : stage + 1;
       wait_vmem(0);  // this wave's loads of tile it have landed
       barrier();     // ... and every wave's; the scratch tile of tile it - 1 is no longer read
       if (more) issue(kt1, mk1, mv1, next_stage);
@@ -576,7 +631,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
         expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      gemm1<false>(w, sparse_k ? scratch : st, lo, hf, lds);
+      gemm1<false>(w, sparse_k ? scratch : st, lo, hf, zp);
       const int shift = kTile * kt0 - kQTile * qt;
       const bool need = softmax_max(w, shift > -kTile, false, shift, r, hf, c);
       const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
@@ -593,42 +648,88 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
       mv0 = mv1;
     }
   } else {
-  bool prev_sparse_v = false;
-  const char *st_prev = lds;
-  int stage = 0;
-  for (int it = 0; it < n_tiles; ++it) {
-    int kt1 = 0, mk1 = 0, mv1 = 0;
-    const bool more = it + 1 < n_tiles;
-    if (more) tile_info(it + 1, kt1, mk1, mv1);
-    const int next_stage = stage == kStages - 1 ? 0 : stage + 1;
-    wait_vmem(0);  // this wave's loads of tile it have landed
-    barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
-    if (more) issue(kt1, mk1, mv1, next_stage);
-
-    const char *st = lds + stage * kStageBytes;
-    const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
-    if (sparse_k)
-      gemm1<true>(w, st, lo, hf, lds);
-    else
-      gemm1<false>(w, st, lo, hf, lds);
-    const int shift = kTile * kt0 - kQTile * qt;
-    const bool need = softmax_max(w, shift > -kTile, kSmfmac && !sparse_v, shift, r, hf, c);
-    const float lsum = exp_and_gemm2(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, lds);
-    softmax_finish(w, need, lsum);
-    prev_sparse_v = sparse_v;
-    st_prev = st;
-    stage = next_stage;
-    kt0 = kt1;
-    mk0 = mk1;
-    mv0 = mv1;
-  }
-  // GEMM2 of the last tile (its stage is not overwritten after the loop).
-  if (n_tiles > 0) {
-    uint2 meta[4];
-    load_vmeta(meta, st_prev, prev_sparse_v, lo, lds);
+    // The tile walk, specialised at compile time when every visible block of the workgroup has
+    // both operands 2:4 (KIND 1) or both dense (KIND 2): the tile kinds are then constants and
+    // the body has no branches on them. KIND 0 tests each tile.
+    auto walk = [&](auto kind_tag) {
+      constexpr int KIND = decltype(kind_tag)::value;
+      auto kinds_of = [&](int mk, int mv, bool &sk, bool &sv) {
+        sk = KIND == 0 ? mk < 0 : KIND == 1;
+        sv = KIND == 0 ? mv < 0 : KIND == 1;
+      };
+      if constexpr (W == 4) {
+        // Two workgroups per CU, two stages: GEMM2 of a tile follows its softmax in the same
+        // step, and the other workgroup's waves on the SIMD fill its dependency waits.
+        int stage = 0;
+        for (int it = 0; it < n_tiles; ++it) {
+          int kt1 = 0, mk1 = 0, mv1 = 0;
+          const bool more = it + 1 < n_tiles;
+          if (more) tile_info(it + 1, kt1, mk1, mv1);
+          wait_vmem(0);  // this wave's loads of tile it have landed
+          barrier();     // ... and every wave's; the other stage (tile it - 1) is no longer read
+          if (more) issue(kt1, mk1, mv1, stage ^ 1);
+          const char *st = lds + stage * kStageBytes;
+          bool sparse_k, sparse_v;
+          kinds_of(mk0, mv0, sparse_k, sparse_v);
+          if (sparse_k)
+            gemm1<true>(w, st, lo, hf, zp);
+          else
+            gemm1<false>(w, st, lo, hf, zp);
+          const int shift = kTile * kt0 - kQTile * qt;
+          const bool need = softmax_max(w, shift > -kTile, !sparse_v, shift, r, hf, c);
+          const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
+          float lsum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) gemm2_smfmac_step(w, st_prev, prev_sparse_v, meta, u, lo, hf);
-  }
+          for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
+          softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
+          gemm2_smfmac(w, st, sparse_v, lo, hf, didx);
+          stage ^= 1;
+          kt0 = kt1;
+          mk0 = mk1;
+          mv0 = mv1;
+        }
+      } else {
+        // One workgroup per CU, three stages: GEMM2 of a tile runs one tile late, beside the
+        // exponentials of the next.
+        bool prev_sparse_v = KIND == 1;
+        const char *st_prev = lds;
+        int stage = 0;
+        for (int it = 0; it < n_tiles; ++it) {
+          int kt1 = 0, mk1 = 0, mv1 = 0;
+          const bool more = it + 1 < n_tiles;
+          if (more) tile_info(it + 1, kt1, mk1, mv1);
+          const int next_stage = stage == NS - 1 ? 0 : stage + 1;
+          wait_vmem(0);  // this wave's loads of tile it have landed
+          barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
+          if (more) issue(kt1, mk1, mv1, next_stage);
+          const char *st = lds + stage * kStageBytes;
+          bool sparse_k, sparse_v;
+          kinds_of(mk0, mv0, sparse_k, sparse_v);
+          if (sparse_k)
+            gemm1<true>(w, st, lo, hf, zp);
+          else
+            gemm1<false>(w, st, lo, hf, zp);
+          const int shift = kTile * kt0 - kQTile * qt;
+          const bool need = softmax_max(w, shift > -kTile, !sparse_v, shift, r, hf, c);
+          const float lsum = exp_and_gemm2(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, didx);
+          softmax_finish(w, need, lsum);
+          prev_sparse_v = sparse_v;
+          st_prev = st;
+          stage = next_stage;
+          kt0 = kt1;
+          mk0 = mk1;
+          mv0 = mv1;
+        }
+        // GEMM2 of the last tile (its stage is not overwritten after the loop).
+        if (n_tiles > 0) gemm2_smfmac(w, st_prev, prev_sparse_v, lo, hf, didx);
+      }
+    };
+    if (kinds == 2)
+      walk(std::integral_constant<int, 1>{});
+    else if (kinds == 1)
+      walk(std::integral_constant<int, 2>{});
+    else
+      walk(std::integral_constant<int, 0>{});
   }
 
   if (!has_task) return;
@@ -649,17 +750,30 @@ __global__ __launch_bounds__(512, 1) void k_prefill(PrefillArgs a) {
   if (a.lse && hf == 0) a.lse[qrow] = l > 0.f ? (w.m_run + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// Workgroups of W waves: each takes W (query head, 32-query tile) tasks of one KV head.
+template <int W>
+void set_grid(PrefillArgs &a, int b) {
+  a.wg_per_head = (a.G * a.nqt + W - 1) / W;
+  a.n_wg = b * a.hkv * a.wg_per_head;
+}
 template <int B, class E>
-hipError_t launch_b(const PrefillArgs &a, bool smfmac, hipStream_t stream) {
-  if (smfmac)
-    k_prefill<B, true, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
-  else
-    k_prefill<B, false, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+hipError_t launch_b(PrefillArgs a, int b, bool smfmac, hipStream_t stream) {
+  if (smfmac && a.nb <= Lay<4, true>::kMaxB) {
+    set_grid<4>(a, b);
+    k_prefill<B, 4, true, E><<<a.n_wg, 4 * 64, 0, stream>>>(a);
+  } else if (smfmac) {
+    set_grid<kWaves>(a, b);
+    k_prefill<B, kWaves, true, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+  } else {
+    set_grid<kWaves>(a, b);
+    k_prefill<B, kWaves, false, E><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 template <class E>
-hipError_t launch_e(const PrefillArgs &a, int block, bool smfmac, hipStream_t stream) {
-  return block == 64 ? launch_b<64, E>(a, smfmac, stream) : launch_b<128, E>(a, smfmac, stream);
+hipError_t launch_e(const PrefillArgs &a, int b, int block, bool smfmac, hipStream_t stream) {
+  return block == 64 ? launch_b<64, E>(a, b, smfmac, stream)
+                     : launch_b<128, E>(a, b, smfmac, stream);
 }
 
 }  // namespace
@@ -677,15 +791,13 @@ hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, 
   a.hq = d.hq;
   a.G = d.G;
   a.nqt = d.L / kQTile;
-  a.wg_per_head = (d.G * a.nqt + kWaves - 1) / kWaves;
-  a.n_wg = d.b * d.hkv * a.wg_per_head;
   a.ndk = d.ndk;
   a.nsk = d.nsk;
   a.ndv = d.ndv;
   a.nsv = d.nsv;
   a.scale_log2 = scale_log2;
-  return d.dtype == kF16 ? launch_e<_Float16>(a, d.B, smfmac, stream)
-                         : launch_e<__bf16>(a, d.B, smfmac, stream);
+  return d.dtype == kF16 ? launch_e<_Float16>(a, d.b, d.B, smfmac, stream)
+                         : launch_e<__bf16>(a, d.b, d.B, smfmac, stream);
 }
 
 }  // namespace hs

@@ -11,7 +11,7 @@ HSP_MFMA_32X32X16, HSP_SMFMAC_32X32X32, HSP_MFMA_16X16X32, HSP_SMFMAC_16X16X64 =
 HSP_VALU_EXP2, HSP_VALU_FMA, HSP_VALU_MAX3, HSP_VALU_CVT, HSP_VALU_SOFTMAX = 0, 1, 2, 3, 4
 HSP_VALU_DOT2 = 5
 
-EXPORTS = ("hsp_matrix_loop", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_lds_read",
+EXPORTS = ("hsp_matrix_loop", "hsp_matrix_chain", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_lds_read",
            "hsp_read")
 
 _lib = None
@@ -26,6 +26,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I = ctypes.c_void_p, ctypes.c_int
         L.hsp_matrix_loop.argtypes = [I, I, I, I, P, P, P]
+        L.hsp_matrix_chain.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_valu_loop.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_wave.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_split.argtypes = [I, I, I, I, P, P, P]
@@ -52,6 +53,11 @@ def _check(rc, what):
 
 def matrix_loop(kind, grid, waves, iters, out, clk=None):
     _check(lib().hsp_matrix_loop(kind, grid, waves, iters, _p(out), _p(clk), _s()), "matrix_loop")
+
+
+def matrix_chain(kind, accumulators, grid, waves, iters, out, clk=None):
+    _check(lib().hsp_matrix_chain(kind, accumulators, grid, waves, iters, _p(out), _p(clk), _s()),
+           "matrix_chain")
 
 
 def valu_loop(op, grid, waves, iters, out, clk=None, chains=8):

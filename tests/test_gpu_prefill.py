@@ -164,3 +164,22 @@ def test_prefill_dense_equals_library_attention():
     vt = torch.from_numpy(synth.bf16_to_f32(V)).repeat_interleave(hq // hkv, dim=1)
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).numpy()
     assert_close(o, ref.astype(np.float64).reshape(-1, 128), tag="prefill dense vs sdpa fp32")
+
+
+@pytest.mark.parametrize("path", ["smfmac", "decompress"])
+def test_prefill_long_head_eight_wave_path(path):
+    """A head of 2049 64-token blocks (131136 tokens): more blocks than the four-wave SMFMAC
+    workgroups list, so the SMFMAC path runs the eight-wave kernel; sampled rows (the tile edges
+    near both ends and random rows) against the oracle."""
+    rng = np.random.default_rng(31)
+    b, hq, hkv, B, nb = 1, 2, 1, 64, 2049
+    L = nb * B
+    counts = (205, 1024, 1024)
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    print(f"[prefill] {path} L={L} (2049 blocks)", flush=True)
+    rows = sample_rows(b, hq, L, 12, 9)
+    o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path],
+                                             rows=rows)
+    assert_close(o, ref, lse, ref_lse, f"{path} L={L}")
