@@ -201,6 +201,20 @@ __device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t
       : "v"(voff), "s"(gbase), "s"(lds_addr)
       : "memory");
 }
+// dma16 with the nontemporal cache policy: for data read once (the decode's stream), so that it
+// does not displace reused lines.
+__device__ __forceinline__ void dma16_nt(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
 __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(

@@ -363,6 +363,35 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
   return lsum;
 }
 
+// GEMM2 of one staged tile in two parts: the operand reads of k-step u (and, for u = 0, the
+// index words of both), and the SMFMACs of k-step u on them, so that the reads can be issued well
+// ahead of the SMFMACs.
+struct VOps {
+  uint2 meta[4];
+  uint4 v0[4], v1[4];
+};
+__device__ __forceinline__ void gemm2_read(VOps &v, const char *st, bool sparse, int u,
+                                           const LaneOffsets &lo, const char *didx) {
+  if (u == 0) load_vmeta(v.meta, st, sparse, lo, didx);
+  const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) v.v0[ct] = lds16(st + off + ct * kCtStride);
+  if (!sparse) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) v.v1[ct] = lds16(st + (off ^ 16) + ct * kCtStride);
+  }
+}
+template <class E>
+__device__ __forceinline__ void gemm2_apply(WaveState<E> &w, const VOps &v, bool sparse, int u,
+                                            int hf) {
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const uint32_t idx = (u ? v.meta[ct].y : v.meta[ct].x) >> (16 * hf);
+    w.o[ct] = smfmac32(as8<E>(v.v0[ct]), w.p[u], idx, w.o[ct]);
+    if (!sparse) w.o[ct] = smfmac32(as8<E>(v.v1[ct]), w.p[u], 0xEEEEu, w.o[ct]);
+  }
+}
+
 // GEMM2 of one staged tile alone.
 template <class E>
 __device__ __forceinline__ void gemm2_smfmac(WaveState<E> &w, const char *st, bool sparse,
@@ -675,6 +704,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
             gemm1<true>(w, st, lo, hf, zp);
           else
             gemm1<false>(w, st, lo, hf, zp);
+          // GEMM2's first operand reads go out before the softmax, whose vector work then covers
+          // their latency.
+          VOps v;
+          gemm2_read(v, st, sparse_v, 0, lo, didx);
+          __builtin_amdgcn_sched_barrier(0);
           const int shift = kTile * kt0 - kQTile * qt;
           const bool need = softmax_max(w, shift > -kTile, !sparse_v, shift, r, hf, c);
           const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
@@ -682,7 +716,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
           softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
-          gemm2_smfmac(w, st, sparse_v, lo, hf, didx);
+          gemm2_apply(w, v, sparse_v, 0, hf);
+          gemm2_read(v, st, sparse_v, 1, lo, didx);
+          gemm2_apply(w, v, sparse_v, 1, hf);
           stage ^= 1;
           kt0 = kt1;
           mk0 = mk1;
