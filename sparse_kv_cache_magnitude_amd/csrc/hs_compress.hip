@@ -90,6 +90,13 @@ __device__ __forceinline__ uint32_t elem(const uint4 &v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// 16-byte load with the nontemporal cache policy: K and V are streamed once per pass.
+typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt(const uint16_t *p) {
+  const u32x4nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4nt *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int B, class E>
 __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
                                                const uint16_t *__restrict__ V,
@@ -105,8 +112,8 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
     uint4 kr[4], vr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      kr[r] = *reinterpret_cast<const uint4 *>(Kb + (size_t)(4 * g + r) * kD + 8 * c8);
-      vr[r] = *reinterpret_cast<const uint4 *>(Vb + (size_t)(4 * g + r) * kD + 8 * c8);
+      kr[r] = ldnt(Kb + (size_t)(4 * g + r) * kD + 8 * c8);
+      vr[r] = ldnt(Vb + (size_t)(4 * g + r) * kD + 8 * c8);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // K: groups of four channels of one token
@@ -282,18 +289,17 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ K,
 
   // K: dense copy, or per token: four groups of four channels -> 8 kept values + 1 meta word.
   if (mk > 0) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(K + base);
     uint4 *dst = reinterpret_cast<uint4 *>(c.k_dense + (size_t)(mk - 1) * BD);
 #pragma unroll
-    for (int e = tid; e < BD / 8; e += 256) dst[e] = src[e];
+    for (int e = tid; e < BD / 8; e += 256) dst[e] = ldnt(K + base + 8 * e);
   } else if (mk < 0) {
     const size_t s = (size_t)(-mk - 1);
     uint16_t *nnz = c.k_nnz + s * (BD / 2), *meta = c.k_meta + s * (BD / 16);
 #pragma unroll
     for (int item = tid; item < B * (kD / 16); item += 256) {
       const int t = item >> 3, w = item & 7;
-      const uint4 *p = reinterpret_cast<const uint4 *>(K + base + (size_t)t * kD + 16 * w);
-      const uint4 x0 = p[0], x1 = p[1];
+      const uint16_t *p = K + base + (size_t)t * kD + 16 * w;
+      const uint4 x0 = ldnt(p), x1 = ldnt(p + 8);
       const uint32_t wd[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t pairs[4], word = 0;
 #pragma unroll
@@ -311,49 +317,51 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ K,
     }
   }
 
-  // V: work item = (four consecutive tokens g, eight consecutive channels c8); the lanes holding
-  // the four token groups of one metadata word are lane, lane^16, lane^32, lane^48.
+  // V: both pools are channel-major (row = one channel's B tokens), the block token-major. The
+  // block goes through LDS (16-byte unit u of token row t at unit u ^ ((t >> 3) & 7), so that the
+  // column reads below hit distinct banks), then each lane emits 16 contiguous bytes of one
+  // channel row: a wave writes 1 KB of consecutive rows at a time.
   if (mv != 0) {
+    __shared__ __attribute__((aligned(16))) uint16_t vt[B * kD];
     const bool dense = mv > 0;
     const size_t s = dense ? (size_t)(mv - 1) : (size_t)(-mv - 1);
+    auto at = [](int t, int ch) { return t * kD + 8 * ((ch >> 3) ^ ((t >> 3) & 7)) + (ch & 7); };
 #pragma unroll
-    for (int item = tid; item < (B / 4) * 16; item += 256) {
-      const int g = item >> 4, c8 = item & 15;
-      uint4 vr[4];
+    for (int idx = tid; idx < B * 16; idx += 256) {
+      const int t = idx >> 4, u = idx & 15;
+      *reinterpret_cast<uint4 *>(vt + at(t, 8 * u)) = ldnt(V + base + (size_t)t * kD + 8 * u);
+    }
+    __syncthreads();
+    if (dense) {
+      uint16_t *dst = c.v_dense + s * BD;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[r] = *reinterpret_cast<const uint4 *>(V + base + (size_t)(4 * g + r) * kD + 8 * c8);
-      if (dense) {
-        uint16_t *dst = c.v_dense + s * BD;
+      for (int idx = tid; idx < kD * (B / 8); idx += 256) {  // (channel, 8 tokens)
+        const int ch = idx / (B / 8), j = idx % (B / 8);
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint2 out = make_uint2(elem(vr[0], e) | (elem(vr[1], e) << 16),
-                                 elem(vr[2], e) | (elem(vr[3], e) << 16));
-          *reinterpret_cast<uint2 *>(dst + (size_t)(8 * c8 + e) * B + 4 * g) = out;
-        }
-      } else {
-        uint16_t *nnz = c.v_nnz + s * (BD / 2), *meta = c.v_meta + s * (BD / 16);
-        uint32_t words[4] = {0, 0, 0, 0};  // metadata words of channels 8*c8 + e, two per dword
+        for (int k = 0; k < 4; ++k)
+          w[k] = (uint32_t)vt[at(8 * j + 2 * k, ch)] | ((uint32_t)vt[at(8 * j + 2 * k + 1, ch)] << 16);
+        *reinterpret_cast<uint4 *>(dst + (size_t)ch * B + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      uint16_t *nnz = c.v_nnz + s * (BD / 2), *meta = c.v_meta + s * (BD / 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t x0 = elem(vr[0], e), x1 = elem(vr[1], e), x2 = elem(vr[2], e),
-                   x3 = elem(vr[3], e);
-          uint32_t nib = mask_to_nibble(
+      for (int idx = tid; idx < kD * (B / 16); idx += 256) {  // (channel, 16 tokens)
+        const int ch = idx / (B / 16), wd = idx % (B / 16);
+        uint32_t pairs[4], word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // groups of four tokens
+          const int t0 = 16 * wd + 4 * q;
+          const uint32_t x0 = vt[at(t0, ch)], x1 = vt[at(t0 + 1, ch)], x2 = vt[at(t0 + 2, ch)],
+                         x3 = vt[at(t0 + 3, ch)];
+          const uint32_t nib = mask_to_nibble(
               keep_mask(x0 & 0x7FFFu, x1 & 0x7FFFu, x2 & 0x7FFFu, x3 & 0x7FFFu));
-          *reinterpret_cast<uint32_t *>(nnz + (size_t)(8 * c8 + e) * (B / 2) + 2 * g) =
-              kept_pair(nib, x0, x1, x2, x3);
-          words[e >> 1] |= nib << (4 * (g & 3) + 16 * (e & 1));
+          pairs[q] = kept_pair(nib, x0, x1, x2, x3);
+          word |= nib << (4 * q);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          words[q] |= __shfl_xor(words[q], 16, 64);
-          words[q] |= __shfl_xor(words[q], 32, 64);
-        }
-        // lane group g & 3 == q stores the words of channels 8*c8 + 2q, 8*c8 + 2q + 1
-        const int q = g & 3;
-        const uint32_t wq = q == 0 ? words[0] : (q == 1 ? words[1] : (q == 2 ? words[2] : words[3]));
-        meta[(size_t)(8 * c8 + 2 * q) * (B / 16) + (g >> 2)] = (uint16_t)(wq & 0xFFFFu);
-        meta[(size_t)(8 * c8 + 2 * q + 1) * (B / 16) + (g >> 2)] = (uint16_t)(wq >> 16);
+        *reinterpret_cast<uint4 *>(nnz + (size_t)ch * (B / 2) + 8 * wd) =
+            make_uint4(pairs[0], pairs[1], pairs[2], pairs[3]);
+        meta[(size_t)ch * (B / 16) + wd] = (uint16_t)word;
       }
     }
   }
