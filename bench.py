@@ -31,7 +31,8 @@ WORKLOAD = "decode_llama8b_32k_b8"
 HBM_PEAK_GBS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 SETTLE_BYTES = 1 << 30  # read pass that settles dirty last-level-cache lines (cache: 256 MiB)
-SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked", "policy", "f16")
+SUITE_PARTS = ("prefill16k", "decode128k", "sweeps", "recompress", "masked", "policy", "f16",
+               "ablation")
 COPY_BYTES = 1 << 30    # calibration copy for the byte counters (--copy-probe)
 COPY_KERNEL = "neg_kernel"  # torch's elementwise kernel that the calibration copy runs
 
@@ -64,7 +65,8 @@ def parse():
                         "is a comma list of " + ", ".join(SUITE_PARTS) + " (default: all): 16K "
                         "prefill with both 2:4 paths, 128K decode, the sparsity sweeps, the "
                         "prefill-to-decode re-compression, the caller-mask compressor, the "
-                        "sink/local dense policy and the fp16 element type at 32K batch 8")
+                        "sink/local dense policy, the fp16 element type at 32K batch 8 and the "
+                        "prefill ablation (each optimisation left out in turn) at 32K batch 8")
     p.add_argument("--peaks", action="store_true",
                    help="instead of the headline step: the measured ceilings of the GPU "
                         "(libhspeaks.so): matrix-core issue loops (MFMA and SMFMAC), vector-ALU "
@@ -362,6 +364,8 @@ def run_suite(parts=SUITE_PARTS, reps=7):
         suite_policy(hs, synth, setup, timed, decode_time, emit)
     if "f16" in parts:
         suite_f16(hs, synth, timed, decode_time, prefill_time, emit, torch)
+    if "ablation" in parts:
+        suite_ablation(hs, synth, setup, timed, emit, torch)
     return 0
 
 
@@ -555,6 +559,41 @@ def suite_f16(hs, synth, timed, decode_time, prefill_time, emit, torch):
           "mfma_utilisation": round(ex / (BF16_DENSE_PEAK_TFLOPS * 1e12) / t_p, 4),
           "compress_us": round(comp * 1e6, 1)})
     del K, V, Q, q
+
+def suite_ablation(hs, synth, setup, timed, emit, torch):
+    """What each optimisation of the SMFMAC prefill is worth (the ablation of the HieraSparse
+    paper's §IV-C, Fig. 4, at its setting: Llama-3.1-8B attention shape, 32K context, batch 8):
+    the default kernel and its variants that leave out one optimisation each (loads pipelined a
+    tile ahead, the dense and 2:4 stage buffers aliased, the walks specialised for all-2:4 and
+    all-dense workgroups, four-wave workgroups two per CU, and the token order that lets P^T stay
+    in registers instead of a round trip through LDS), on the decode workload's mixed cache
+    (25% dense, 60% 2:4, 15% pruned blocks) and on an all-2:4 cache."""
+    base = synth.workload(WORKLOAD)
+    variants = (("default", hs.HS_PREFILL_VARIANT_NONE),
+                ("sync_loads", hs.HS_PREFILL_VARIANT_SYNC_LOADS),
+                ("no_alias", hs.HS_PREFILL_VARIANT_NO_ALIAS),
+                ("generic_walk", hs.HS_PREFILL_VARIANT_GENERIC_WALK),
+                ("lockstep_8wave", hs.HS_PREFILL_VARIANT_LOCKSTEP),
+                ("lds_relayout", hs.HS_PREFILL_VARIANT_LDS_RELAYOUT))
+    gains = {"sync_loads": "gain_pipelining", "no_alias": "gain_aliasing",
+             "generic_walk": "gain_specialised_walk", "lockstep_8wave": "gain_four_wave",
+             "lds_relayout": "gain_in_register_relayout"}
+    for tag, counts in (("mixed", None), ("all24", (0, base.nb, base.nb))):
+        w = base if counts is None else base.with_counts(*counts)
+        K, V, Q, q, shp, cnt, cache, _ = setup(w)
+        del K, V, q
+        O = torch.empty_like(Q)
+        ms = {}
+        for name, v in variants:
+            ms[name] = timed(lambda: hs.hs_prefill_attn_variant(shp, cnt, cache, Q, O, None, 0.0,
+                                                                v)) * 1e3
+        rec = {"suite": f"ablation_prefill_32k_b8_{tag}",
+               "counts": [w.n_p, w.n_sk, w.n_sv]}
+        rec.update({f"{n}_ms": round(t, 3) for n, t in ms.items()})
+        rec.update({g: round(ms[n] / ms["default"], 3) for n, g in gains.items()})
+        emit(rec)
+        del Q, O, cache
+
 
 def run_peaks(reps=3):
     """Measured ceilings of the GPU. Each probe is timed with HIP events (median of `reps` after

@@ -10,6 +10,7 @@
  *                    log-sum-exp combine step and GQA packing.
  *   hs_prefill_attn  [HS] §III-C Algorithm 1 with the mixed dense/sparse dispatch of §III-C2,
  *                    made causal, skipping pruned blocks.
+ *   hs_prefill_attn_variant  the prefill with one optimisation of [HS] §IV-C left out (Fig. 4).
  *   hs_recompress    [HS] §III, Fig. 3: the cache compressed again with other block counts (e.g.
  *                    K dense and V 2:4 for prefill, then both 2:4 for decode).
  *   hs_compress_masked  [HS] §III-A cache pruner fed by any pruning algorithm's block-level and
@@ -219,6 +220,28 @@ hs_status hs_decode_attn_noalloc(const hs_shape *shape, const hs_counts *counts,
 hs_status hs_prefill_attn(const hs_shape *shape, const hs_counts *counts, const hs_cache *cache,
                           const uint16_t *q, uint16_t *o, float *lse, float softmax_scale,
                           uint32_t flags, void *stream);
+
+/* Variants of the SMFMAC prefill that each leave out one of its optimisations, for measuring
+   what every optimisation is worth (the ablation of [HS] §IV-C, Fig. 4). Same arguments, outputs
+   and results (up to the order of fp32 sums for LOCKSTEP and LDS_RELAYOUT) as hs_prefill_attn
+   with HS_PREFILL_SMFMAC, for bf16 heads of at most 2048 blocks, 1024 for LDS_RELAYOUT
+   (HS_ERR_UNSUPPORTED otherwise, or for another variant code). */
+enum {
+  HS_PREFILL_VARIANT_NONE = 0,         /* the SMFMAC kernel hs_prefill_attn runs */
+  HS_PREFILL_VARIANT_SYNC_LOADS = 1,   /* no pipelining: a tile's loads are issued and waited for
+                                          in the step that computes on it (§IV-C1) */
+  HS_PREFILL_VARIANT_NO_ALIAS = 2,     /* dense and 2:4 forms of a stage in separate LDS buffers,
+                                          so one workgroup per CU (§IV-C3) */
+  HS_PREFILL_VARIANT_GENERIC_WALK = 4, /* no walk specialised for all-2:4 or all-dense workgroups
+                                          (§IV-C3) */
+  HS_PREFILL_VARIANT_LOCKSTEP = 8,     /* one eight-wave workgroup per CU, GEMM2 one tile late */
+  HS_PREFILL_VARIANT_LDS_RELAYOUT = 16 /* K staged in token order, so P^T reaches GEMM2's operand
+                                          layout through a round trip in LDS instead of being
+                                          produced in place (§IV-C2, Fig. 5) */
+};
+hs_status hs_prefill_attn_variant(const hs_shape *shape, const hs_counts *counts,
+                                  const hs_cache *cache, const uint16_t *q, uint16_t *o,
+                                  float *lse, float softmax_scale, uint32_t variant, void *stream);
 
 /* Static description of a status code. */
 const char *hs_status_string(hs_status status);

@@ -397,6 +397,36 @@ HS_API hs_status hs_prefill_attn(const hs_shape *shape, const hs_counts *counts,
   return ok();
 }
 
+HS_API hs_status hs_prefill_attn_variant(const hs_shape *shape, const hs_counts *counts,
+                                         const hs_cache *cache, const uint16_t *q, uint16_t *o,
+                                         float *lse, float softmax_scale, uint32_t variant,
+                                         void *stream) {
+  hs::Dims d;
+  hs::CacheView c;
+  hs_status st = make_dims(shape, counts, &d);
+  if (st) return st;
+  if ((st = check_cache(cache, d, &c))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse", false)))
+    return st;
+  if (variant != HS_PREFILL_VARIANT_NONE && variant != HS_PREFILL_VARIANT_SYNC_LOADS &&
+      variant != HS_PREFILL_VARIANT_NO_ALIAS && variant != HS_PREFILL_VARIANT_GENERIC_WALK &&
+      variant != HS_PREFILL_VARIANT_LOCKSTEP && variant != HS_PREFILL_VARIANT_LDS_RELAYOUT)
+    return fail(HS_ERR_UNSUPPORTED, "unknown prefill variant %u", variant);
+  if (d.dtype != hs::kBf16 || d.nb > (variant == HS_PREFILL_VARIANT_LDS_RELAYOUT ? 1024 : 2048))
+    return fail(HS_ERR_UNSUPPORTED,
+                "prefill variants take bf16 heads of at most 2048 blocks (1024 for variant 16)");
+  static_assert(HS_PREFILL_VARIANT_SYNC_LOADS == hs::kPrefillVariantSyncLoads &&
+                    HS_PREFILL_VARIANT_NO_ALIAS == hs::kPrefillVariantNoAlias &&
+                    HS_PREFILL_VARIANT_GENERIC_WALK == hs::kPrefillVariantGenericWalk &&
+                    HS_PREFILL_VARIANT_LOCKSTEP == hs::kPrefillVariantLockstep &&
+                    HS_PREFILL_VARIANT_LDS_RELAYOUT == hs::kPrefillVariantLdsRelayout,
+                "variant codes");
+  hipError_t e = hs::launch_prefill_variant(d, c, q, o, lse, scale_log2(softmax_scale, d.D),
+                                            (int)variant, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 HS_API const char *hs_status_string(hs_status s) {
   switch (s) {
     case HS_OK: return "ok";

@@ -46,6 +46,15 @@ hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, u
 hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
                           float *lse, float scale_log2, bool smfmac, hipStream_t stream);
 
+// Ablation variants of the SMFMAC prefill (hs_prefill_attn_variant): bf16, heads of at most 2048
+// blocks (1024 for the LDS re-layout); hipErrorInvalidValue otherwise.
+constexpr int kPrefillVariantSyncLoads = 1, kPrefillVariantNoAlias = 2,
+              kPrefillVariantGenericWalk = 4, kPrefillVariantLockstep = 8,
+              kPrefillVariantLdsRelayout = 16;
+hipError_t launch_prefill_variant(const Dims &d, const CacheView &c, const uint16_t *q,
+                                  uint16_t *o, float *lse, float scale_log2, int variant,
+                                  hipStream_t stream);
+
 // Dense stand-ins of a compressed cache: K, V [b][hkv][L][D] with kept values in place and zeros
 // elsewhere (hs_recompress.hip).
 hipError_t launch_unpack(const Dims &d, const CacheView &c, uint16_t *k_out, uint16_t *v_out,

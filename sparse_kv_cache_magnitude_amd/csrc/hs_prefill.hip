@@ -87,20 +87,34 @@ constexpr int kVMetaOff = kRegion + 2048;  // stage: 2:4 V metadata
 //              -(i+1) 2:4 slot i); kListBlk their block indices (int16); kMaxB entries each
 //   kScratch   decompress path: the dense image of the current tile's 2:4 operands (the stage
 //              layout, K at 0, V^T at kRegion), expanded once per tile by the whole workgroup
-template <int W, bool kSmfmac>
+// Ablation variants of the SMFMAC path (measurement only; the library's entry points run A = 0):
+constexpr int kAblSyncLoads = 1;    // a tile's loads are issued and waited for in its own step
+constexpr int kAblNoAlias = 2;      // a stage holds separate dense and 2:4 buffers (64 KB)
+constexpr int kAblGenericWalk = 4;  // no walk specialised on the operand kinds
+constexpr int kAblLdsRelayout = 16;  // K rows in token order, P^T re-laid out through LDS
+static_assert(kAblSyncLoads == kPrefillVariantSyncLoads && kAblNoAlias == kPrefillVariantNoAlias &&
+                  kAblGenericWalk == kPrefillVariantGenericWalk &&
+                  kAblLdsRelayout == kPrefillVariantLdsRelayout,
+              "variant codes");
+template <int W, bool kSmfmac, int A = 0>
 struct Lay {
   static constexpr int kStagesN = (kSmfmac && W == 4) ? 2 : 3;
-  static constexpr int kMaxB = W == 4 ? 2048 : kMaxBlocks;
-  static constexpr int kDenseIdx = kStagesN * kStageBytes;
+  // (the LDS re-layout variant lists 1024 blocks, to keep its P^T buffers within 80 KB)
+  static constexpr int kMaxB = W == 4 ? ((A & kAblLdsRelayout) ? 1024 : 2048) : kMaxBlocks;
+  // Without aliasing, the 2:4 representation of a tile sits kSparse bytes above its dense one.
+  static constexpr int kSparse = (A & kAblNoAlias) ? kStageBytes : 0;
+  static constexpr int kStride = kStageBytes + kSparse;  // bytes between stages
+  static constexpr int kDenseIdx = kStagesN * kStride;
   static constexpr int kZero = kDenseIdx + 1024;
   static constexpr int kCount = kZero + 128;
   static constexpr int kKind = kCount + 4 * W;
   static constexpr int kListModes = (kKind + 4 * W + 15) / 16 * 16;
   static constexpr int kListBlk = kListModes + 4 * kMaxB;
-  static constexpr int kEnd = kListBlk + 2 * kMaxB;
+  static constexpr int kPBuf = kListBlk + 2 * kMaxB;  // 2 KB per wave (LDS re-layout variant)
+  static constexpr int kEnd = kPBuf + ((A & kAblLdsRelayout) ? 2048 * W : 0);
   static constexpr int kScratch = (kEnd + 1023) / 1024 * 1024;
   static constexpr int kBytes = kSmfmac ? kEnd : kScratch + kStageBytes;
-  static_assert(kBytes <= (W == 4 ? 80 : 160) * 1024, "LDS budget");
+  static_assert(kBytes <= ((W == 4 && !(A & kAblNoAlias)) ? 80 : 160) * 1024, "LDS budget");
 };
 static_assert(kRegion % 1024 == 0 && kMetaOff % 1024 == 0, "whole 1 KB loads per region");
 
@@ -276,16 +290,18 @@ __device__ __forceinline__ void gemm2_dense_step(WaveState<E> &w, const char *st
 // ---- softmax of the current tile: causal mask, running max, decision to rescale ----------------
 // 'shift' = (first token of the key tile) - (first query of the wave); a token is masked when
 // shift + token > query. Returns true if the running max moves (then w.alpha rescales O and l).
-template <class E>
+// kNatural: the K rows are staged in token order (no tau).
+template <bool kNatural = false, class E>
 __device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool split, int shift, int r,
                                             int hf, float c) {
   if (diag) {
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (shift + 32 * T + tau(8 * (e >> 2) + 4 * hf + (e & 3), split) > r)
-          w.s[T][e] = -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int row = 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (shift + 32 * T + (kNatural ? row : tau(row, split)) > r) w.s[T][e] = -INFINITY;
+      }
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -392,6 +408,39 @@ __device__ __forceinline__ void gemm2_apply(WaveState<E> &w, const VOps &v, bool
   }
 }
 
+// Measurement variant without the token order tau: the K rows are staged in token order, so the
+// accumulator register pair jp of lane half hf (per 32-token half) holds tokens
+// nat = 8 (jp >> 1) + 4 hf + 2 (jp & 1), while GEMM2's B operand wants tau(nat) there. P^T is
+// moved through this wave's 2 KB of LDS: row q (the lane's query) of 32 tokens, its 16-byte unit
+// x stored at x ^ ((q >> 2) & 3); pairs written at their own token, read at tau's.
+template <class E>
+__device__ __forceinline__ void relayout_through_lds(WaveState<E> &w, int u, char *scr, bool split,
+                                                     int q, int hf) {
+  auto at = [&](int t) { return scr + 64 * q + 16 * ((t >> 3) ^ ((q >> 2) & 3)) + 2 * (t & 7); };
+  {
+    const uint4 a = __builtin_bit_cast(uint4, half8<E>(w.p[u], 0)),
+                b = __builtin_bit_cast(uint4, half8<E>(w.p[u], 1));
+    const uint32_t pr[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)  // pairs 2g, 2g + 1: tokens 8 g + 4 hf .. + 3
+      *reinterpret_cast<uint2 *>(at(8 * g + 4 * hf)) = make_uint2(pr[2 * g], pr[2 * g + 1]);
+    uint4 ra, rb;
+    if (!split) {  // tau = swap23: pairs 0..3 are tokens 8 hf .. + 7, pairs 4..7 16 more
+      ra = lds16(at(8 * hf));
+      rb = lds16(at(16 + 8 * hf));
+    } else {
+      uint32_t rd[8];
+#pragma unroll
+      for (int jp = 0; jp < 8; ++jp)
+        rd[jp] = *reinterpret_cast<const uint32_t *>(at(swap13(8 * (jp >> 1) + 4 * hf + 2 * (jp & 1))));
+      ra = make_uint4(rd[0], rd[1], rd[2], rd[3]);
+      rb = make_uint4(rd[4], rd[5], rd[6], rd[7]);
+    }
+    w.p[u] = __builtin_shufflevector(as8<E>(ra), as8<E>(rb), 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                     12, 13, 14, 15);
+  }
+}
+
 // GEMM2 of one staged tile alone.
 template <class E>
 __device__ __forceinline__ void gemm2_smfmac(WaveState<E> &w, const char *st, bool sparse,
@@ -440,9 +489,10 @@ __device__ __forceinline__ void expand_tile(const char *st, char *dst, bool spar
 // by wave 1; V: one 1 KB load by wave 2 (block 64), or four 256 B dword loads by waves 3-6
 // (block 128, where a tile is half of each channel's metadata row).
 
-template <int B, int W, bool kSmfmac, class E>
+template <int B, int W, bool kSmfmac, class E, int A = 0>
 __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs a) {
-  using L = Lay<W, kSmfmac>;
+  using L = Lay<W, kSmfmac, A>;
+  constexpr int SP = L::kSparse;  // offset of a stage's 2:4 buffers from its dense ones
   static_assert(kSmfmac || W == kWaves, "the decompress path runs eight waves");
   __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hf = lane >> 5;
@@ -566,7 +616,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
   {
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
-      auto token = [&](int slot) { return (slot & ~31) | tau(slot & 31, sp); };
+      auto token = [&](int slot) {
+        return (A & kAblLdsRelayout) ? slot : (slot & ~31) | tau(slot & 31, sp);
+      };
       const int rd = 4 * wave + (lane >> 4), cd = lane & 15;   // dense K: 16 units per row
       oKd[sp] = token(rd) * 256 + 16 * (cd ^ (rd & 15));
       const int rn = 8 * wave + (lane >> 3), cn = lane & 7;    // 2:4 K: 8 units per row
@@ -592,7 +644,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
   const uint16_t *vm_h = a.c.v_meta + (size_t)head * a.nsv * B * (kD / 16);
   auto issue = [&](int kt, int mk, int mv, int stage) {
     const int half = kt % TPB;
-    const uint32_t kl = lds_base + stage * kStageBytes, vl = kl + kRegion;
+    const uint32_t kl = lds_base + stage * L::kStride, vl = kl + kRegion;
+    const uint32_t ksl = kl + SP, vsl = vl + SP;  // 2:4 buffers
     const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
     if (mk > 0) {
       const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
@@ -604,9 +657,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
       const uint32_t o = sp ? oKn[1] : oKn[0];
 #pragma unroll
-      for (int i = 0; i < 8 / W; ++i) dma16(g + i * (8 * W) * kD, o, kl + 1024 * (wave + W * i));
+      for (int i = 0; i < 8 / W; ++i) dma16(g + i * (8 * W) * kD, o, ksl + 1024 * (wave + W * i));
       if (wave == 1)
-        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], kl + kMetaOff);
+        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], ksl + kMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
@@ -619,13 +672,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
 #pragma unroll
       for (int i = 0; i < 8 / W; ++i) {
         const int q = wave + W * i;
-        dma16(g + i * (16 * W) * B, oVn, vl + (q >> 1) * kCtStride + 1024 * (q & 1));
+        dma16(g + i * (16 * W) * B, oVn, vsl + (q >> 1) * kCtStride + 1024 * (q & 1));
       }
       const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
       if (B == 64) {
-        if (wave == 2) dma16(gm, oVm, kl + kVMetaOff);
+        if (wave == 2) dma16(gm, oVm, ksl + kVMetaOff);
       } else if (wave >= kVmWave0 && wave < kVmWave0 + 4) {
-        dma4(gm, oVm, kl + kVMetaOff + 256 * (wave - kVmWave0));
+        dma4(gm, oVm, ksl + kVMetaOff + 256 * (wave - kVmWave0));
       }
     }
   };
@@ -654,7 +707,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       barrier();     // ... and every wave's; the scratch tile of tile it - 1 is no longer read
       if (more) issue(kt1, mk1, mv1, next_stage);
 
-      const char *st = lds + stage * kStageBytes;
+      const char *st = lds + stage * L::kStride;
       const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
       if (sparse_k || sparse_v) {
         expand_tile<E>(st, scratch, sparse_k, sparse_v, tid);
@@ -694,30 +747,46 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           int kt1 = 0, mk1 = 0, mv1 = 0;
           const bool more = it + 1 < n_tiles;
           if (more) tile_info(it + 1, kt1, mk1, mv1);
-          wait_vmem(0);  // this wave's loads of tile it have landed
-          barrier();     // ... and every wave's; the other stage (tile it - 1) is no longer read
-          if (more) issue(kt1, mk1, mv1, stage ^ 1);
-          const char *st = lds + stage * kStageBytes;
+          if constexpr ((A & kAblSyncLoads) != 0) {
+            // ablation: the tile's own loads, waited for at once (no overlap with computing)
+            if (it > 0) issue(kt0, mk0, mv0, stage);
+            wait_vmem(0);
+            barrier();
+          } else {
+            wait_vmem(0);  // this wave's loads of tile it have landed
+            barrier();     // ... and every wave's; the other stage (tile it - 1) is no longer read
+            if (more) issue(kt1, mk1, mv1, stage ^ 1);
+          }
+          const char *st = lds + stage * L::kStride;
           bool sparse_k, sparse_v;
           kinds_of(mk0, mv0, sparse_k, sparse_v);
           if (sparse_k)
-            gemm1<true>(w, st, lo, hf, zp);
+            gemm1<true>(w, st + SP, lo, hf, zp);
           else
             gemm1<false>(w, st, lo, hf, zp);
+          const char *sv = sparse_v ? st + SP : st;
           // GEMM2's first operand reads go out before the softmax, whose vector work then covers
           // their latency.
           VOps v;
-          gemm2_read(v, st, sparse_v, 0, lo, didx);
+          gemm2_read(v, sv, sparse_v, 0, lo, didx);
           __builtin_amdgcn_sched_barrier(0);
           const int shift = kTile * kt0 - kQTile * qt;
-          const bool need = softmax_max(w, shift > -kTile, !sparse_v, shift, r, hf, c);
+          constexpr bool kNat = (A & kAblLdsRelayout) != 0;
+          const bool need = softmax_max<kNat>(w, shift > -kTile, !sparse_v, shift, r, hf, c);
           const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
           float lsum = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) softmax_exp(w, ks, c, mc, lsum);
+          for (int ks = 0; ks < 4; ++ks) {
+            softmax_exp(w, ks, c, mc, lsum);
+            if constexpr (kNat) {
+              if (ks & 1)
+                relayout_through_lds(w, ks >> 1, lds + L::kPBuf + 2048 * wave, !sparse_v,
+                                     lane & 31, hf);
+            }
+          }
           softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
           gemm2_apply(w, v, sparse_v, 0, hf);
-          gemm2_read(v, st, sparse_v, 1, lo, didx);
+          gemm2_read(v, sv, sparse_v, 1, lo, didx);
           gemm2_apply(w, v, sparse_v, 1, hf);
           stage ^= 1;
           kt0 = kt1;
@@ -738,16 +807,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           wait_vmem(0);  // this wave's loads of tile it have landed
           barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
           if (more) issue(kt1, mk1, mv1, next_stage);
-          const char *st = lds + stage * kStageBytes;
+          const char *st = lds + stage * L::kStride;
           bool sparse_k, sparse_v;
           kinds_of(mk0, mv0, sparse_k, sparse_v);
           if (sparse_k)
-            gemm1<true>(w, st, lo, hf, zp);
+            gemm1<true>(w, st + SP, lo, hf, zp);
           else
             gemm1<false>(w, st, lo, hf, zp);
           const int shift = kTile * kt0 - kQTile * qt;
           const bool need = softmax_max(w, shift > -kTile, !sparse_v, shift, r, hf, c);
-          const float lsum = exp_and_gemm2(w, st_prev, it > 0, prev_sparse_v, lo, hf, c, didx);
+          const char *sv_prev = prev_sparse_v ? st_prev + SP : st_prev;
+          const float lsum = exp_and_gemm2(w, sv_prev, it > 0, prev_sparse_v, lo, hf, c, didx);
           softmax_finish(w, need, lsum);
           prev_sparse_v = sparse_v;
           st_prev = st;
@@ -757,12 +827,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           mv0 = mv1;
         }
         // GEMM2 of the last tile (its stage is not overwritten after the loop).
-        if (n_tiles > 0) gemm2_smfmac(w, st_prev, prev_sparse_v, lo, hf, didx);
+        if (n_tiles > 0)
+          gemm2_smfmac(w, prev_sparse_v ? st_prev + SP : st_prev, prev_sparse_v, lo, hf, didx);
       }
     };
-    if (kinds == 2)
+    if (kinds == 2 && !(A & kAblGenericWalk))
       walk(std::integral_constant<int, 1>{});
-    else if (kinds == 1)
+    else if (kinds == 1 && !(A & kAblGenericWalk))
       walk(std::integral_constant<int, 2>{});
     else
       walk(std::integral_constant<int, 0>{});
@@ -806,6 +877,35 @@ hipError_t launch_b(PrefillArgs a, int b, bool smfmac, hipStream_t stream) {
   }
   return hipGetLastError();
 }
+// Ablation variants of the SMFMAC path, bf16 (measurement only).
+template <int B>
+hipError_t launch_variant_b(PrefillArgs a, int b, int variant, hipStream_t stream) {
+  if (variant == kPrefillVariantLockstep) {
+    set_grid<kWaves>(a, b);
+    k_prefill<B, kWaves, true, __bf16><<<a.n_wg, kWaves * 64, 0, stream>>>(a);
+    return hipGetLastError();
+  }
+  set_grid<4>(a, b);
+  switch (variant) {
+    case 0: k_prefill<B, 4, true, __bf16><<<a.n_wg, 256, 0, stream>>>(a); break;
+    case kAblSyncLoads:
+      k_prefill<B, 4, true, __bf16, kAblSyncLoads><<<a.n_wg, 256, 0, stream>>>(a);
+      break;
+    case kAblNoAlias:
+      k_prefill<B, 4, true, __bf16, kAblNoAlias><<<a.n_wg, 256, 0, stream>>>(a);
+      break;
+    case kAblGenericWalk:
+      k_prefill<B, 4, true, __bf16, kAblGenericWalk><<<a.n_wg, 256, 0, stream>>>(a);
+      break;
+    case kAblLdsRelayout:
+      if (a.nb > Lay<4, true, kAblLdsRelayout>::kMaxB) return hipErrorInvalidValue;
+      k_prefill<B, 4, true, __bf16, kAblLdsRelayout><<<a.n_wg, 256, 0, stream>>>(a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <class E>
 hipError_t launch_e(const PrefillArgs &a, int b, int block, bool smfmac, hipStream_t stream) {
   return block == 64 ? launch_b<64, E>(a, b, smfmac, stream)
@@ -814,8 +914,9 @@ hipError_t launch_e(const PrefillArgs &a, int b, int block, bool smfmac, hipStre
 
 }  // namespace
 
-hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
-                          float *lse, float scale_log2, bool smfmac, hipStream_t stream) {
+namespace {
+PrefillArgs prefill_args(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
+                         float *lse, float scale_log2) {
   PrefillArgs a;
   a.c = c;
   a.q = q;
@@ -832,8 +933,24 @@ hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, 
   a.ndv = d.ndv;
   a.nsv = d.nsv;
   a.scale_log2 = scale_log2;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_prefill(const Dims &d, const CacheView &c, const uint16_t *q, uint16_t *o,
+                          float *lse, float scale_log2, bool smfmac, hipStream_t stream) {
+  const PrefillArgs a = prefill_args(d, c, q, o, lse, scale_log2);
   return d.dtype == kF16 ? launch_e<_Float16>(a, d.b, d.B, smfmac, stream)
                          : launch_e<__bf16>(a, d.b, d.B, smfmac, stream);
+}
+
+hipError_t launch_prefill_variant(const Dims &d, const CacheView &c, const uint16_t *q,
+                                  uint16_t *o, float *lse, float scale_log2, int variant,
+                                  hipStream_t stream) {
+  if (d.dtype != kBf16 || d.nb > Lay<4, true>::kMaxB) return hipErrorInvalidValue;
+  const PrefillArgs a = prefill_args(d, c, q, o, lse, scale_log2);
+  return d.B == 64 ? launch_variant_b<64>(a, d.b, variant, stream)
+                   : launch_variant_b<128>(a, d.b, variant, stream);
 }
 
 }  // namespace hs

@@ -17,10 +17,14 @@ HS_ERR_WORKSPACE, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_OVERLAP = 5, 6, 7, 8
 HS_OP_COMPRESS, HS_OP_DECODE, HS_OP_RECOMPRESS = 1, 2, 3
 HS_BF16, HS_F16 = 0, 1
 HS_PREFILL_SMFMAC, HS_PREFILL_DECOMPRESS = 0, 1
+# Prefill variants of hs_prefill_attn_variant (one optimisation of the SMFMAC prefill left out).
+(HS_PREFILL_VARIANT_NONE, HS_PREFILL_VARIANT_SYNC_LOADS, HS_PREFILL_VARIANT_NO_ALIAS,
+ HS_PREFILL_VARIANT_GENERIC_WALK, HS_PREFILL_VARIANT_LOCKSTEP,
+ HS_PREFILL_VARIANT_LDS_RELAYOUT) = 0, 1, 2, 4, 8, 16
 
 EXPORTS = ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
            "hs_compress_masked", "hs_recompress", "hs_decode_attn", "hs_decode_attn_noalloc",
-           "hs_prefill_attn", "hs_status_string", "hs_last_error")
+           "hs_prefill_attn", "hs_prefill_attn_variant", "hs_status_string", "hs_last_error")
 
 # Bytes of the device array hs_decode_attn_noalloc uses (HS_DECODE_NOALLOC_SCRATCH_BYTES).
 HS_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -81,9 +85,10 @@ def lib():
                                              ctypes.c_float, ctypes.c_int32, P]
         L.hs_prefill_attn.argtypes = [S(HsShape), S(HsCounts), S(HsCache), P, P, P,
                                       ctypes.c_float, ctypes.c_uint32, P]
+        L.hs_prefill_attn_variant.argtypes = L.hs_prefill_attn.argtypes
         for f in ("hs_cache_sizes", "hs_workspace_size", "hs_compress", "hs_compress_ex",
                   "hs_compress_masked", "hs_recompress", "hs_decode_attn",
-                  "hs_decode_attn_noalloc", "hs_prefill_attn"):
+                  "hs_decode_attn_noalloc", "hs_prefill_attn", "hs_prefill_attn_variant"):
             getattr(L, f).restype = ctypes.c_int
         L.hs_status_string.argtypes = [ctypes.c_int]
         L.hs_status_string.restype = ctypes.c_char_p
@@ -200,6 +205,14 @@ def hs_prefill_attn(shp, cnt, cache, q, o, lse=None, softmax_scale=0.0,
     _check(lib().hs_prefill_attn(ctypes.byref(shp), ctypes.byref(cnt),
                                  ctypes.byref(_cache_struct(cache)), _ptr(q), _ptr(o), _ptr(lse),
                                  float(softmax_scale), int(flags), _stream(stream)))
+
+
+def hs_prefill_attn_variant(shp, cnt, cache, q, o, lse=None, softmax_scale=0.0,
+                            variant=HS_PREFILL_VARIANT_NONE, stream=None):
+    _check(lib().hs_prefill_attn_variant(ctypes.byref(shp), ctypes.byref(cnt),
+                                         ctypes.byref(_cache_struct(cache)), _ptr(q), _ptr(o),
+                                         _ptr(lse), float(softmax_scale), int(variant),
+                                         _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------------

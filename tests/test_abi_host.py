@@ -90,6 +90,7 @@ def test_bad_shapes_rejected_by_every_entry_point(shp, code):
     assert _status(lambda: _compress(shp, cnt, FAKE, FAKE, cache, FAKE, 1 << 30)) == code
     assert _status(lambda: _decode(shp, cnt, cache, FAKE, FAKE, None, 0, FAKE, 1 << 30)) == code
     assert _status(lambda: _prefill(shp, cnt, cache, FAKE, FAKE, None, 0)) == code
+    assert _status(lambda: _prefill_variant(shp, cnt, cache, FAKE, FAKE, None, 0)) == code
     assert hs.hs_last_error() != ""
 
 
@@ -132,6 +133,12 @@ def _prefill(shp, cnt, cache, q, o, lse, flags):
     _raise(hs.lib().hs_prefill_attn(ctypes.byref(shp), ctypes.byref(cnt),
                                     ctypes.byref(_cache_struct(cache)), q, o, lse, 0.0, flags,
                                     None))
+
+
+def _prefill_variant(shp, cnt, cache, q, o, lse, variant):
+    _raise(hs.lib().hs_prefill_attn_variant(ctypes.byref(shp), ctypes.byref(cnt),
+                                            ctypes.byref(_cache_struct(cache)), q, o, lse, 0.0,
+                                            variant, None))
 
 
 SHP, CNT = hs.shape(1, 4, 1, 1024, 128, 64), hs.counts(2, 4, 5)
@@ -279,6 +286,26 @@ def test_unknown_flags_and_ops():
     cache = {f: FAKE for f in hs.CACHE_FIELDS}
     assert _status(lambda: _prefill(SHP, CNT, cache, FAKE, FAKE, None, 7)) == hs.HS_ERR_UNSUPPORTED
     assert _status(lambda: hs.hs_workspace_size(9, SHP, CNT)) == hs.HS_ERR_UNSUPPORTED
+
+
+def test_prefill_variant_validation():
+    cache = {f: FAKE for f in hs.CACHE_FIELDS}
+    for v in (3, 5, 32, 0xFFFFFFFF):
+        assert _status(lambda: _prefill_variant(SHP, CNT, cache, FAKE, FAKE, None, v)) == \
+            hs.HS_ERR_UNSUPPORTED
+    # fp16 elements and heads of more than 2048 blocks have no variants
+    f16 = hs.shape(1, 4, 1, 1024, 128, 64, dtype=hs.HS_F16)
+    assert _status(lambda: _prefill_variant(f16, CNT, cache, FAKE, FAKE, None, 1)) == \
+        hs.HS_ERR_UNSUPPORTED
+    long_head = hs.shape(1, 4, 1, 64 * 2049, 128, 64)
+    assert _status(lambda: _prefill_variant(long_head, hs.counts(0, 0, 0), cache, FAKE, FAKE,
+                                            None, 2)) == hs.HS_ERR_UNSUPPORTED
+    assert "variant" in hs.hs_last_error()
+    mid_head = hs.shape(1, 4, 1, 64 * 1025, 128, 64)
+    assert _status(lambda: _prefill_variant(mid_head, hs.counts(0, 0, 0), cache, FAKE, FAKE,
+                                            None, 16)) == hs.HS_ERR_UNSUPPORTED
+    assert _status(lambda: _prefill_variant(SHP, CNT, cache, None, FAKE, None, 0)) == \
+        hs.HS_ERR_NULL
 
 
 def test_status_strings():

@@ -20,7 +20,7 @@ FLAGS = {"smfmac": hs.HS_PREFILL_SMFMAC, "decompress": hs.HS_PREFILL_DECOMPRESS}
 
 
 def run_prefill(b, hq, hkv, L, B, counts, K, V, Q, flags, scale=0.0, cache=None, want=None,
-                rows=None):
+                rows=None, variant=None):
     """GPU causal prefill over the GPU compression of K, V and the oracle's over the oracle's
     compression (checked equal); rows: flat indices into [b][hq][L] to compare (None = all).
     Returns (o, lse, ref, ref_lse, cache, want) with o, lse restricted to the rows."""
@@ -32,7 +32,10 @@ def run_prefill(b, hq, hkv, L, B, counts, K, V, Q, flags, scale=0.0, cache=None,
     qd = gu.to_dev(Q)
     o = torch.empty((b, hq, L, 128), dtype=torch.int16, device="cuda")
     lse = torch.empty((b, hq, L), dtype=torch.float32, device="cuda")
-    hs.hs_prefill_attn(shp, cnt, cache, qd, o, lse, scale, flags)
+    if variant is None:
+        hs.hs_prefill_attn(shp, cnt, cache, qd, o, lse, scale, flags)
+    else:
+        hs.hs_prefill_attn_variant(shp, cnt, cache, qd, o, lse, scale, variant)
     torch.cuda.synchronize()
     of = synth.bf16_to_f32(gu.to_host_u16(o)).reshape(-1, 128)
     lf = lse.cpu().numpy().reshape(-1)
@@ -183,3 +186,35 @@ def test_prefill_long_head_eight_wave_path(path):
     o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, FLAGS[path],
                                              rows=rows)
     assert_close(o, ref, lse, ref_lse, f"{path} L={L}")
+
+
+VARIANTS = {"sync_loads": hs.HS_PREFILL_VARIANT_SYNC_LOADS,
+            "no_alias": hs.HS_PREFILL_VARIANT_NO_ALIAS,
+            "generic_walk": hs.HS_PREFILL_VARIANT_GENERIC_WALK,
+            "lockstep": hs.HS_PREFILL_VARIANT_LOCKSTEP,
+            "lds_relayout": hs.HS_PREFILL_VARIANT_LDS_RELAYOUT}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("B,counts", [(64, (0, 16, 16)), (64, (3, 9, 5)), (64, (0, 0, 0)),
+                                      (128, (1, 5, 2)), (128, (0, 8, 8))])
+def test_prefill_ablation_variants(variant, B, counts):
+    """The measurement variants of the SMFMAC prefill (each with one optimisation left out) against
+    the oracle. The variants that only change where and when operands are staged, or which copy of
+    the tile body runs, compute every product and sum of the default kernel in the same order:
+    their outputs equal its outputs bit for bit. The eight-wave variant issues GEMM2 one tile late,
+    and the LDS re-layout variant gives each lane other tokens to sum, so they are held to the
+    oracle only."""
+    rng = np.random.default_rng(B * 7 + sum(counts))
+    b, hq, hkv, L = 2, 8, 2, 16 * 64 if B == 64 else 8 * 128
+    K = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    V = synth.bf16_bits(rng.standard_normal((b, hkv, L, 128), dtype=np.float32))
+    Q = synth.bf16_bits(rng.standard_normal((b, hq, L, 128), dtype=np.float32))
+    print(f"[prefill variant] {variant} B={B} counts={counts}", flush=True)
+    o0, l0, _, _, cache, want = run_prefill(b, hq, hkv, L, B, counts, K, V, Q,
+                                            hs.HS_PREFILL_SMFMAC)
+    o, lse, ref, ref_lse, _, _ = run_prefill(b, hq, hkv, L, B, counts, K, V, Q, None,
+                                             cache=cache, want=want, variant=VARIANTS[variant])
+    assert_close(o, ref, lse, ref_lse, f"{variant} B={B} {counts}")
+    if variant not in ("lockstep", "lds_relayout"):
+        assert np.array_equal(o, o0) and np.array_equal(lse, l0)
