@@ -146,8 +146,9 @@ def measured_traffic(kernel_key, digest):
 
 def summarize_counters(fetch_dir, write_dir):
     """HBM bytes per launch of the hot-path kernels from two rocprofv3 --pmc runs (FETCH_SIZE and
-    WRITE_SIZE, KiB per dispatch). Each counter is scaled by the bytes the calibration copy really
-    moves over what the same counter reads for it. Writes profiles/traffic.json."""
+    WRITE_SIZE, KiB per dispatch), over the launches of each kernel's largest grid. Each counter is
+    scaled by the bytes the calibration copy really moves over what the same counter reads for
+    it. Writes profiles/traffic.json."""
     import csv
     import glob
     from collections import defaultdict
@@ -157,18 +158,24 @@ def summarize_counters(fetch_dir, write_dir):
         if not paths:
             raise SystemExit(f"no counter_collection.csv under {d}")
         vals = defaultdict(lambda: defaultdict(float))
+        grid = {}
         for path in paths:
             with open(path) as f:
                 for r in csv.DictReader(f):
                     if r["Counter_Name"] == counter:
                         vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        out = {}
+                        grid[r["Dispatch_Id"]] = int(r["Grid_Size"])
+        # per kernel, the launches of the largest grid: the headline workload's (the small
+        # workload the bench also times runs the same kernels)
+        launches = defaultdict(list)
         for name, per_dispatch in vals.items():
             key = next((k for k in list(TRAFFIC_KERNELS) + [COPY_KERNEL] if k in name), None)
             if key:
-                v = list(per_dispatch.values())
-                prev = out.get(key, [])
-                out[key] = prev + v
+                launches[key] += [(grid[d], v) for d, v in per_dispatch.items()]
+        out = {}
+        for key, gv in launches.items():
+            top = max(g for g, _ in gv)
+            out[key] = [v for g, v in gv if g == top]
         return out
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
