@@ -877,7 +877,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre_exec_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("k_prefill", source_digest(
                          "hs_prefill.hip", "hs_device.h"))},
-        "roofline_decode": {"bound": "hbm", "kernel": "k_decode_split",
+        "roofline_decode": {"bound": "hbm", "kernel": "k_decode_split+k_decode_combine",
                             "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("k_decode_split", source_digest(

@@ -15,9 +15,9 @@
 //     online softmax per query column (exp2 domain), P^T packed to bf16 in place
 //     O^T += V^T P^T dense block: 16 MFMA over the channel-major copy; 2:4 block: 8 SMFMAC
 //   Every split writes its normalised partial o (fp32) and log-sum-exp to the workspace.
-// k_decode_combine: a second launch on the same stream; merges the splits of each (batch entry,
-//   KV head, column group) by their log-sum-exp and writes o (bf16) and lse. With one split the
-//   split kernel writes o and lse itself and nothing else is launched.
+// k_decode_combine: a second launch on the same stream, one wave per (batch entry, query head);
+//   merges that head's splits by their log-sum-exp and writes o (bf16) and lse. With one split
+//   the split kernel writes o and lse itself and nothing else is launched.
 //
 // LDS tile layout (unpadded, 32 KB per stage): K rows are stored in the MFMA row order
 // (tile_token), V^T rows in channel order. The 16-byte units of every row are XOR-swizzled by a
@@ -88,86 +88,48 @@ __device__ __forceinline__ void wait_tile(int n) {
   }
 }
 
-// Merge the splits of ncol query heads (partial rows row0 + c * splits + s; output rows orow0 + c)
-// by their log-sum-exps: o = sum_s e^(lse_s - m) o_s / sum_s e^(lse_s - m), lse = m + log(sum).
-// Lane l owns channels 4 (l % 32) .. +3 and the splits of parity l / 32, four query heads at a
-// time. Padding entries (heads past ncol, splits past the end) read a valid row with weight 0, so
-// every load is unconditional and one round of loads covers four heads.
+// Merge the splits of one query head's row (partial rows row * splits + s) by their log-sum-exps:
+// o = sum_s e^(lse_s - m) o_s / sum_s e^(lse_s - m), lse = m + log(sum). Lane l owns channels
+// 2 l, 2 l + 1. Each round of up to 64 splits keeps split s's weight in lane s, and its partial
+// rows are loaded eight at a time, all before any is used; loads past the last split read the last
+// split's row with weight 0, so every load is unconditional.
 template <class E>
-__device__ __forceinline__ void combine(const DecodeArgs &a, size_t row0, size_t orow0, int ncol,
-                                        int lane) {
-  const int S = a.splits, q4 = lane & 31, hh = lane >> 5;
-  for (int c0 = 0; c0 < ncol; c0 += 4) {
-    const float *pl[4];
-    const float *pc[4];
-    float mx[4], wsum[4];
-    f32x4 acc[4];
+__device__ __forceinline__ void combine_row(const DecodeArgs &a, size_t row, int lane) {
+  const int S = a.splits;
+  const float *pl = a.part_lse + row * S;
+  const float *po = a.part_o + row * S * kD + 2 * lane;
+  const float ls0 = pl[min(lane, S - 1)];  // log-sum-exps of splits 0 .. 63
+  float mx = lane < S ? ls0 : -INFINITY;
+  for (int s0 = 64; s0 < S; s0 += 64)
+    if (s0 + lane < S) mx = fmaxf(mx, pl[s0 + lane]);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const size_t r = row0 + (size_t)min(c0 + cc, ncol - 1) * S;
-      pl[cc] = a.part_lse + r;
-      pc[cc] = a.part_o + r * kD + 4 * q4;
-      mx[cc] = -INFINITY;
-      wsum[cc] = 0.f;
-      acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    float ls0[4];  // log-sum-exps of splits 0 .. 63, kept for the weights below
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int ns = min(64, S - s0);
+    const float ls = s0 == 0 ? ls0 : pl[s0 + min(lane, ns - 1)];
+    // an empty split (no visible token) has lse -inf and weight 0
+    const float wl = lane < ns && ls != -INFINITY ? __expf(ls - mx) : 0.f;
+    for (int k0 = 0; k0 < ns; k0 += 8) {
+      float2 v[8];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) mx[cc] = ls0[cc] = pl[cc][min(lane, S - 1)];
-    for (int s0 = 64; s0 < S; s0 += 64) {
-      const int sl = min(s0 + lane, S - 1);
+      for (int k = 0; k < 8; ++k)
+        v[k] = *reinterpret_cast<const float2 *>(po + (size_t)(s0 + min(k0 + k, ns - 1)) * kD);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) mx[cc] = fmaxf(mx[cc], pl[cc][sl]);
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mx[cc] = fmaxf(mx[cc], __shfl_xor(mx[cc], o, 64));
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const int ns = min(64, S - s0), sl = min(lane, ns - 1);
-      float wl[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const float ls = s0 == 0 ? ls0[cc] : pl[cc][s0 + sl];
-        const bool use = c0 + cc < ncol && lane < ns && ls != -INFINITY;
-        wl[cc] = use ? __expf(ls - mx[cc]) : 0.f;
+      for (int k = 0; k < 8; ++k) {
+        const float w = k0 + k < ns ? __builtin_bit_cast(
+                                          float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, wl), k0 + k))
+                                    : 0.f;
+        wsum += w;
+        acc0 += w * v[k].x;
+        acc1 += w * v[k].y;
       }
-      for (int k0 = 0; 2 * k0 < ns; k0 += 4) {  // 8 splits (4 per lane half) per round
-        float4 v[4][4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const int sp = min(2 * (k0 + kk) + hh, ns - 1);  // past the end: weight 0 below
-            v[kk][cc] = *reinterpret_cast<const float4 *>(pc[cc] + (size_t)(s0 + sp) * kD);
-          }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const int sr = 2 * (k0 + kk) + hh;
-            const float w = __shfl(wl[cc], min(sr, ns - 1), 64) * (sr < ns ? 1.f : 0.f);
-            wsum[cc] += w;
-            acc[cc] += w * f32x4{v[kk][cc].x, v[kk][cc].y, v[kk][cc].z, v[kk][cc].w};
-          }
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      wsum[cc] += __shfl_xor(wsum[cc], 32, 64);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[cc][i] += __shfl_xor(acc[cc][i], 32, 64);
-      if (c0 + cc >= ncol) continue;
-      const float inv = wsum[cc] > 0.f ? 1.f / wsum[cc] : 0.f;
-      const size_t orow = orow0 + c0 + cc;
-      if (hh == 0)
-        *reinterpret_cast<uint2 *>(a.o + orow * kD + 4 * q4) =
-            make_uint2(pack2<E>(acc[cc][0] * inv, acc[cc][1] * inv),
-                       pack2<E>(acc[cc][2] * inv, acc[cc][3] * inv));
-      if (a.lse && lane == 0)
-        a.lse[orow] = wsum[cc] > 0.f ? mx[cc] + __logf(wsum[cc]) : -INFINITY;
     }
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *reinterpret_cast<uint32_t *>(a.o + row * kD + 2 * lane) = pack2<E>(acc0 * inv, acc1 * inv);
+  if (a.lse && lane == 0) a.lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
 template <int B, class E>
@@ -432,15 +394,12 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   if (g == 0) a.part_lse[row] = lse_s;
 }
 
-// ---- log-sum-exp combine of the splits, §IV-C: one wave per (batch entry, KV head, column group)
-// merges the partials the split kernel left in the workspace. It is a second launch on the same
-// stream, so the stream order alone makes every split's partials visible to it.
+// ---- log-sum-exp combine of the splits, §IV-C: one wave per (batch entry, query head) merges the
+// partials the split kernel left in the workspace. It is a second launch on the same stream, so the
+// stream order alone makes every split's partials visible to it.
 template <class E>
 __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
-  const int h = blockIdx.y % a.hkv, cg = blockIdx.y / a.hkv, bi = blockIdx.z;
-  const int hq0 = h * a.G + 16 * cg, ncol = min(16, a.G - 16 * cg);
-  combine<E>(a, ((size_t)bi * a.hq + hq0) * a.splits, (size_t)bi * a.hq + hq0, ncol,
-             threadIdx.x);
+  combine_row<E>(a, blockIdx.x, threadIdx.x);
 }
 
 }  // namespace
@@ -454,7 +413,7 @@ hipError_t launch_decode(const Dims &d, const CacheView &c, const uint16_t *q, u
   DecodeArgs a{c, q, o, lse, part_o, part_lse, d.nb, total_w, d.hkv, d.hq, d.G, splits,
                scale_log2};
   const int col_groups = (d.G + 15) / 16;
-  const dim3 grid(splits, d.hkv * col_groups, d.b), grid_c(1, d.hkv * col_groups, d.b);
+  const dim3 grid(splits, d.hkv * col_groups, d.b), grid_c(d.b * d.hq);
   if (d.dtype == kF16) {
     if (d.B == 64)
       k_decode_split<64, _Float16><<<grid, 64, 0, stream>>>(a);
