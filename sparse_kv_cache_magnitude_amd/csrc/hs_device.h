@@ -227,6 +227,59 @@ __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t 
       : "v"(voff), "s"(gbase), "s"(lds_addr)
       : "memory");
 }
+// N (1, 2 or 4) direct loads of one lane pattern: load i reads 16 bytes per lane at g[i] + voff
+// into LDS m0 + 1024-byte slot, m0 = lds0 + i * lstride. M0 is saved once and restored once for the
+// run (one load per M0 write, with the one wait state an M0 write needs before a direct load).
+template <int N>
+__device__ __forceinline__ void dma16_run(const char *const (&g)[N], uint32_t voff, uint32_t lds0,
+                                          uint32_t lstride) {
+  uint32_t saved;
+  if constexpr (N == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds0), "s"(g[0])
+        : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_add_u32 m0, m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds0), "s"(lstride), "s"(g[0]), "s"(g[1])
+        : "memory");
+  } else {
+    static_assert(N == 4, "runs of 1, 2 or 4 loads");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_add_u32 m0, m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "s_add_u32 m0, m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "s_add_u32 m0, m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %7\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds0), "s"(lstride), "s"(g[0]), "s"(g[1]), "s"(g[2]), "s"(g[3])
+        : "memory");
+  }
+}
+
 // Wait until at most n of this wave's vector-memory operations are outstanding (n in 0..24; larger
 // values wait for all).
 __device__ __forceinline__ void wait_vmem(int n) {

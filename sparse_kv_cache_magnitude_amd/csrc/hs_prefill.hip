@@ -119,6 +119,7 @@ struct Lay {
 static_assert(kRegion % 1024 == 0 && kMetaOff % 1024 == 0, "whole 1 KB loads per region");
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr float kLazyBound = 256.0f;  // 2^kTau: no probability above it while the max holds
 
 
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
@@ -289,20 +290,23 @@ __device__ __forceinline__ void gemm2_dense_step(WaveState<E> &w, const char *st
 
 // ---- softmax of the current tile: causal mask, running max, decision to rescale ----------------
 // 'shift' = (first token of the key tile) - (first query of the wave); a token is masked when
-// shift + token > query. Returns true if the running max moves (then w.alpha rescales O and l).
-// kNatural: the K rows are staged in token order (no tau).
+// shift + token > query. kNatural: the K rows are staged in token order (no tau).
 template <bool kNatural = false, class E>
-__device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool split, int shift, int r,
-                                            int hf, float c) {
-  if (diag) {
+__device__ __forceinline__ void softmax_mask(WaveState<E> &w, bool split, int shift, int r, int hf) {
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+  for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = 8 * (e >> 2) + 4 * hf + (e & 3);
-        if (shift + 32 * T + (kNatural ? row : tau(row, split)) > r) w.s[T][e] = -INFINITY;
-      }
-  }
+    for (int e = 0; e < 16; ++e) {
+      const int row = 8 * (e >> 2) + 4 * hf + (e & 3);
+      if (shift + 32 * T + (kNatural ? row : tau(row, split)) > r) w.s[T][e] = -INFINITY;
+    }
+}
+
+// The tile's row maxima against the running max: returns true if the running max moves (by more
+// than kTau; then w.alpha rescales O and l and w.m_use is the new max), else w.m_use = the running
+// max.
+template <class E>
+__device__ __forceinline__ bool softmax_rescale(WaveState<E> &w, float c) {
   float mx = -INFINITY;
 #pragma unroll
   for (int T = 0; T < 2; ++T)
@@ -319,6 +323,13 @@ __device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool spl
     w.m_use = w.m_run;
   }
   return need;
+}
+
+template <bool kNatural = false, class E>
+__device__ __forceinline__ bool softmax_max(WaveState<E> &w, bool diag, bool split, int shift, int r,
+                                            int hf, float c) {
+  if (diag) softmax_mask<kNatural>(w, split, shift, r, hf);
+  return softmax_rescale(w, c);
 }
 
 // P^T of the current tile for GEMM2 k-step ks (16 tokens): the accumulator registers
@@ -650,30 +661,37 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
     if (mk > 0) {
       const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
       const uint32_t o = sp ? oKd[1] : oKd[0];
+      const char *gr[16 / W];
 #pragma unroll
-      for (int i = 0; i < 16 / W; ++i) dma16(g + i * (4 * W) * 2 * kD, o, kl + 1024 * (wave + W * i));
+      for (int i = 0; i < 16 / W; ++i) gr[i] = g + i * (4 * W) * 2 * kD;
+      dma16_run<16 / W>(gr, o, kl + 1024 * wave, 1024 * W);
     } else {
       const int row0 = (-mk - 1) * B + kTile * half;
       const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
       const uint32_t o = sp ? oKn[1] : oKn[0];
+      const char *gs[8 / W];
 #pragma unroll
-      for (int i = 0; i < 8 / W; ++i) dma16(g + i * (8 * W) * kD, o, ksl + 1024 * (wave + W * i));
+      for (int i = 0; i < 8 / W; ++i) gs[i] = g + i * (8 * W) * kD;
+      dma16_run<8 / W>(gs, o, ksl + 1024 * wave, 1024 * W);
       if (wave == 1)
         dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], ksl + kMetaOff);
     }
     if (mv > 0) {
       const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
+      const char *gr[16 / W];
 #pragma unroll
-      for (int i = 0; i < 16 / W; ++i) dma16(g + i * (8 * W) * 2 * B, oVd, vl + 1024 * (wave + W * i));
+      for (int i = 0; i < 16 / W; ++i) gr[i] = g + i * (8 * W) * 2 * B;
+      dma16_run<16 / W>(gr, oVd, vl + 1024 * wave, 1024 * W);
     } else {
       const int blk = (-mv - 1) * B * kD;
       const char *g = uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half);
-      // 16 rows per load; rows 32 ct + .. start at ct * kCtStride.
+      // 16 rows per load; load q = wave + W i covers rows 16 q .., and rows 32 ct + .. start at
+      // ct * kCtStride: LDS offset (q >> 1) kCtStride + 1024 (q & 1), a step of W / 2 groups per i.
+      const char *gs[8 / W];
 #pragma unroll
-      for (int i = 0; i < 8 / W; ++i) {
-        const int q = wave + W * i;
-        dma16(g + i * (16 * W) * B, oVn, vsl + (q >> 1) * kCtStride + 1024 * (q & 1));
-      }
+      for (int i = 0; i < 8 / W; ++i) gs[i] = g + i * (16 * W) * B;
+      dma16_run<8 / W>(gs, oVn, vsl + (wave >> 1) * kCtStride + 1024 * (wave & 1),
+                       (W / 2) * kCtStride);
       const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
       if (B == 64) {
         if (wave == 2) dma16(gm, oVm, ksl + kVMetaOff);
@@ -733,6 +751,49 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
     // The tile walk, specialised at compile time when every visible block of the workgroup has
     // both operands 2:4 (KIND 1) or both dense (KIND 2): the tile kinds are then constants and
     // the body has no branches on them. KIND 0 tests each tile.
+    // Causal mask, running max, exponentials and row sums of the tile in w.s (key tile kt, V of
+    // the tile 2:4 or not); P^T lands in w.p and O, l are rescaled if the max moves.
+    auto softmax_tile = [&](int kt, bool sparse_v) __attribute__((always_inline)) {
+      const int shift = kTile * kt - kQTile * qt;
+      constexpr bool kNat = (A & kAblLdsRelayout) != 0;
+      if (shift > -kTile) softmax_mask<kNat>(w, !sparse_v, shift, r, hf);
+      auto exps = [&]() __attribute__((always_inline)) {
+        const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
+        float ls = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          softmax_exp(w, ks, c, mc, ls);
+          if constexpr (kNat) {
+            if (ks & 1)
+              relayout_through_lds(w, ks >> 1, lds + L::kPBuf + 2048 * wave, !sparse_v,
+                                   lane & 31, hf);
+          }
+        }
+        return ls;
+      };
+      // The exponentials are taken against the running max first. The tile's maxima are needed
+      // only while a row has no max yet, or when a row's probabilities could exceed 2^kTau,
+      // which the sum of a lane's 32 of them reveals; then the max may move and the exponentials
+      // are taken again against the new one.
+      bool need;
+      float lsum;
+      // (the LDS re-layout variant always takes the tile max first: its round trip leaves no
+      // registers for a second copy of the exponentials)
+      if (kNat || __builtin_amdgcn_ballot_w64(w.m_run == -INFINITY) != 0) {
+        need = softmax_rescale(w, c);
+        lsum = exps();
+      } else {
+        w.m_use = w.m_run;
+        w.alpha = 1.f;
+        lsum = exps();
+        need = false;
+        if (__builtin_amdgcn_ballot_w64(lsum > kLazyBound) != 0) {
+          need = softmax_rescale(w, c);
+          if (need) lsum = exps();
+        }
+      }
+      softmax_finish(w, need, lsum);
+    };
     auto walk = [&](auto kind_tag) {
       constexpr int KIND = decltype(kind_tag)::value;
       auto kinds_of = [&](int mk, int mv, bool &sk, bool &sv) {
@@ -770,21 +831,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           VOps v;
           gemm2_read(v, sv, sparse_v, 0, lo, didx);
           __builtin_amdgcn_sched_barrier(0);
-          const int shift = kTile * kt0 - kQTile * qt;
-          constexpr bool kNat = (A & kAblLdsRelayout) != 0;
-          const bool need = softmax_max<kNat>(w, shift > -kTile, !sparse_v, shift, r, hf, c);
-          const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;
-          float lsum = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            softmax_exp(w, ks, c, mc, lsum);
-            if constexpr (kNat) {
-              if (ks & 1)
-                relayout_through_lds(w, ks >> 1, lds + L::kPBuf + 2048 * wave, !sparse_v,
-                                     lane & 31, hf);
-            }
-          }
-          softmax_finish(w, need, lsum);  // O rescaled before this tile's P V^T is added
+          softmax_tile(kt0, sparse_v);  // O rescaled before this tile's P V^T is added
           gemm2_apply(w, v, sparse_v, 0, hf);
           gemm2_read(v, sv, sparse_v, 1, lo, didx);
           gemm2_apply(w, v, sparse_v, 1, hf);
