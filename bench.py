@@ -731,7 +731,7 @@ def run_peaks(reps=3):
     rout = torch.empty(4096 * 256, device=dev, dtype=torch.int32)
     if os.environ.get("HSP_SKIP_READ"):
         return 0
-    for mode, tag in ((0, "registers"), (1, "direct_to_lds")):
+    for mode, tag in ((0, "registers_nt"), (1, "direct_to_lds"), (2, "direct_to_lds_nt")):
         for g in (512, 1024, 2048, 4096):
             t = timed(lambda: pk.read(mode, src, g, rout))
             emit({"peak": "read", "path": tag, "workgroups": g, "bytes": nbytes,

@@ -79,8 +79,9 @@ int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, float *out, 
 int hsp_lds_read(int grid, int waves, int iters, float *out, uint64_t *clk, void *stream);
 
 /* Streaming read of 'bytes' (a multiple of 16 * 64 * 8) from 'src': mode 0 = 16-byte loads into
-   registers, each workgroup one contiguous chunk; mode 1 = the same chunks through direct
-   global->LDS loads (global_load_lds_dwordx4), the loads the attention kernels stage tiles with.
+   registers (nontemporal), each workgroup one contiguous chunk; mode 1 = the same chunks through
+   direct global->LDS loads (global_load_lds_dwordx4), the loads the attention kernels stage tiles
+   with, default cache policy; mode 2 = mode 1 with the nontemporal policy (the decode's loads).
    Workgroups of 256 threads; out: grid * 256 uint32. */
 int hsp_read(int mode, const void *src, size_t bytes, int grid, uint32_t *out, void *stream);
 

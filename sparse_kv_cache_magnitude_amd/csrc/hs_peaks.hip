@@ -260,6 +260,7 @@ __global__ __launch_bounds__(256) void k_read_regs(const u32x4 *src, size_t chun
 
 // Direct loads into LDS: each wave keeps two batches of eight 1 KB loads in flight (16 KB of LDS
 // per wave, never read).
+template <bool kNT>
 __global__ __launch_bounds__(256) void k_read_lds(const char *src, size_t chunk, uint32_t *out) {
   __shared__ __attribute__((aligned(1024))) char lds[4 * 16384];
   const int lane = threadIdx.x & 63;
@@ -271,8 +272,12 @@ __global__ __launch_bounds__(256) void k_read_lds(const char *src, size_t chunk,
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      hs::dma16(hs::uniform_ptr(base + off + 4096 * u), 16 * lane,
-                lds_base + wave * 16384 + half * 8192 + 1024 * u);
+      if constexpr (kNT)
+        hs::dma16_nt(hs::uniform_ptr(base + off + 4096 * u), 16 * lane,
+                     lds_base + wave * 16384 + half * 8192 + 1024 * u);
+      else
+        hs::dma16(hs::uniform_ptr(base + off + 4096 * u), 16 * lane,
+                  lds_base + wave * 16384 + half * 8192 + 1024 * u);
     half ^= 1;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -397,7 +402,9 @@ HSP_API int hsp_read(int mode, const void *src, size_t bytes, int grid, uint32_t
   if (mode == 0)
     k_read_regs<<<grid, 256, 0, s>>>((const u32x4 *)src, chunk / 16, out);
   else if (mode == 1)
-    k_read_lds<<<grid, 256, 0, s>>>((const char *)src, chunk, out);
+    k_read_lds<false><<<grid, 256, 0, s>>>((const char *)src, chunk, out);
+  else if (mode == 2)
+    k_read_lds<true><<<grid, 256, 0, s>>>((const char *)src, chunk, out);
   else
     return -1;
   return status(hipGetLastError());
