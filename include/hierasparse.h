@@ -80,7 +80,7 @@ typedef enum {
   HS_ERR_COUNTS = 3,      /* negative counts or n_pruned + n_sparse_x > nb */
   HS_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   HS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hs_workspace_size() */
-  HS_ERR_UNSUPPORTED = 6, /* valid request this build does not implement (e.g. flags) */
+  HS_ERR_UNSUPPORTED = 6, /* valid request the library does not implement (e.g. flags) */
   HS_ERR_HIP = 7,         /* a HIP launch failed; hs_last_error() has the HIP message */
   HS_ERR_OVERLAP = 8      /* hs_recompress: input, output and workspace memory overlap */
 } hs_status;
