@@ -171,11 +171,13 @@ __global__ __launch_bounds__(256) void k_score(const uint16_t *__restrict__ K,
 
 constexpr int kRankThreads = 1024;
 
-// Ascending bitonic sort of (key, idx) pairs of length n (a power of two) in LDS.
-__device__ void bitonic_sort(uint64_t *key, uint16_t *idx, int n) {
+// Ascending bitonic sort of (key, idx) pairs of length n (a power of two) in LDS by 'nthreads'
+// threads of the workgroup (thread number 'th' among them); every thread of the workgroup calls it
+// with the same n, so the barriers match.
+__device__ void bitonic_sort(uint64_t *key, uint16_t *idx, int n, int th, int nthreads) {
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < n / 2; t += kRankThreads) {
+      for (int t = th; t < n / 2; t += nthreads) {
         int a = (t / j) * 2 * j + (t % j), b = a + j;
         bool up = (a & k) == 0;
         uint64_t ka = key[a], kb = key[b];
@@ -199,10 +201,10 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restric
                                                        int n_p, int n_sk, int n_sv, int dense_lo,
                                                        int dense_hi, int32_t *__restrict__ map_k,
                                                        int32_t *__restrict__ map_v) {
-  __shared__ uint64_t skey[kMaxBlocks];
-  __shared__ uint16_t sidx[kMaxBlocks];
+  __shared__ uint64_t skey[2][kMaxBlocks];
+  __shared__ uint16_t sidx[2][kMaxBlocks];
   __shared__ uint8_t mode[2][kMaxBlocks];  // 0 pruned, 1 dense, 2 2:4
-  __shared__ int scan[2][kRankThreads];
+  __shared__ int scan[4][kRankThreads];
   const int hd = blockIdx.x, tid = threadIdx.x;
   const uint64_t *hk = keys + (size_t)hd * nb * 3;
   int n = 2;
@@ -212,55 +214,69 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restric
   // (a kept-dense block carries the largest key, which no real loss reaches).
   auto ranked = [&](int t) { return t < nb && t >= dense_lo && t < dense_hi; };
   for (int t = tid; t < n; t += kRankThreads) {
-    skey[t] = ranked(t) ? hk[3 * t + 2] : ~0ull;
-    sidx[t] = (uint16_t)t;
+    skey[0][t] = ranked(t) ? hk[3 * t + 2] : ~0ull;
+    sidx[0][t] = (uint16_t)t;
   }
   __syncthreads();
-  bitonic_sort(skey, sidx, n);
+  bitonic_sort(skey[0], sidx[0], n, tid, kRankThreads);
   for (int t = tid; t < nb; t += kRankThreads) {
     uint8_t m = t < n_p ? 0 : 1;
-    mode[0][sidx[t]] = m;
-    mode[1][sidx[t]] = m;
+    mode[0][sidx[0][t]] = m;
+    mode[1][sidx[0][t]] = m;
   }
   __syncthreads();
 
   // Eq. (2d) per tensor among the survivors: the n_s smallest 2:4 losses become 2:4. Pruned
   // blocks carry the largest key, which no real loss reaches (|x| < 2^24 keeps losses < 2^63).
+  // K (x = 0) and V (x = 1) are sorted at once, each by half of the workgroup.
+  for (int x = 0; x < 2; ++x)
+    for (int t = tid; t < n; t += kRankThreads) {
+      skey[x][t] = (ranked(t) && mode[x][t] != 0) ? hk[3 * t + x] : ~0ull;
+      sidx[x][t] = (uint16_t)t;
+    }
+  __syncthreads();
+  {
+    constexpr int kHalf = kRankThreads / 2;
+    const int x = tid / kHalf;
+    bitonic_sort(skey[x], sidx[x], n, tid % kHalf, kHalf);
+  }
   for (int x = 0; x < 2; ++x) {
     const int want = x ? n_sv : n_sk;
-    for (int t = tid; t < n; t += kRankThreads) {
-      skey[t] = (ranked(t) && mode[x][t] != 0) ? hk[3 * t + x] : ~0ull;
-      sidx[t] = (uint16_t)t;
-    }
-    __syncthreads();
-    bitonic_sort(skey, sidx, n);
-    for (int t = tid; t < want; t += kRankThreads) mode[x][sidx[t]] = 2;
-    __syncthreads();
+    for (int t = tid; t < want; t += kRankThreads) mode[x][sidx[x][t]] = 2;
   }
+  __syncthreads();
 
-  // Pool slots in block order: exclusive prefix counts of dense and 2:4 blocks.
+  // Pool slots in block order: exclusive prefix counts of dense and 2:4 blocks, both tensors in
+  // one scan (counters: K dense, K 2:4, V dense, V 2:4).
   constexpr int kPer = kMaxBlocks / kRankThreads;
-  for (int x = 0; x < 2; ++x) {
-    const int ns = x ? n_sv : n_sk, nd = nb - n_p - ns;
-    int cd = 0, cs = 0;
-    for (int e = 0; e < kPer; ++e) {
-      int i = tid * kPer + e;
-      if (i < nb) {
-        cd += mode[x][i] == 1;
-        cs += mode[x][i] == 2;
+  int cnt[4] = {0, 0, 0, 0};
+  for (int e = 0; e < kPer; ++e) {
+    int i = tid * kPer + e;
+    if (i < nb) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        cnt[2 * x] += mode[x][i] == 1;
+        cnt[2 * x + 1] += mode[x][i] == 2;
       }
     }
-    scan[0][tid] = cd;
-    scan[1][tid] = cs;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) scan[c][tid] = cnt[c];
+  __syncthreads();
+  for (int off = 1; off < kRankThreads; off <<= 1) {
+    int v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = tid >= off ? scan[c][tid - off] : 0;
     __syncthreads();
-    for (int off = 1; off < kRankThreads; off <<= 1) {
-      int vd = tid >= off ? scan[0][tid - off] : 0, vs = tid >= off ? scan[1][tid - off] : 0;
-      __syncthreads();
-      scan[0][tid] += vd;
-      scan[1][tid] += vs;
-      __syncthreads();
-    }
-    int rd = scan[0][tid] - cd + hd * nd, rs = scan[1][tid] - cs + hd * ns;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) scan[c][tid] += v[c];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int ns = x ? n_sv : n_sk, nd = nb - n_p - ns;
+    int rd = scan[2 * x][tid] - cnt[2 * x] + hd * nd;
+    int rs = scan[2 * x + 1][tid] - cnt[2 * x + 1] + hd * ns;
     int32_t *map = (x ? map_v : map_k) + (size_t)hd * nb;
     for (int e = 0; e < kPer; ++e) {
       int i = tid * kPer + e;
@@ -269,7 +285,6 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(const uint64_t *__restric
         map[i] = m == 0 ? 0 : (m == 1 ? ++rd : -(++rs));
       }
     }
-    __syncthreads();
   }
 }
 
