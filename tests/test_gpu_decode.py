@@ -71,7 +71,7 @@ def test_decode_workloads(name):
     assert_close(o, ref, lse, ref_lse, name)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 0, 64, 100, 512])
+@pytest.mark.parametrize("splits", [1, 2, 7, 0, 8, 16, 64, 100, 512])
 def test_decode_split_invariance(splits):
     rng = np.random.default_rng(5)
     b, hq, hkv, L, B = 2, 8, 2, 64 * 37, 64
