@@ -831,7 +831,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           VOps v;
           gemm2_read(v, sv, sparse_v, 0, lo, didx);
           __builtin_amdgcn_sched_barrier(0);
+          // The wave runs its matrix phase (GEMM2 of this tile, GEMM1 of the next) at raised
+          // priority, so that when both waves of a SIMD can issue, the matrix instruction goes
+          // first and the softmax of the other wave fills the matrix core's busy cycles.
+          __builtin_amdgcn_s_setprio(0);
           softmax_tile(kt0, sparse_v);  // O rescaled before this tile's P V^T is added
+          __builtin_amdgcn_s_setprio(1);
           gemm2_apply(w, v, sparse_v, 0, hf);
           gemm2_read(v, sv, sparse_v, 1, lo, didx);
           gemm2_apply(w, v, sparse_v, 1, hf);
