@@ -204,6 +204,7 @@ struct WaveState {
 struct LaneOffsets {
   int kd, kn, km;       // dense K; 2:4 K values; 2:4 K metadata (16 B each)
   int vd, vdd, vn, vm;  // dense V^T split (SMFMAC) and dense (decompress); 2:4 V^T; metadata
+  uint32_t vsel;        // byte selector: the lane half's 16-bit index words of both k-steps
 };
 
 // ---- GEMM1: S^T = K Q^T for one staged tile ---------------------------------------------------
@@ -211,9 +212,8 @@ struct LaneOffsets {
 // k-step over 16-channel chunk cc takes the Q registers half8(qv[cc & 3], cc >> 2). The 2:4 step s
 // covers chunks s and s + 4: lane half hf holds the kept values of chunk s + 4hf, whose 16-bit
 // metadata word is half s & 1 of dword (s >> 1) + 2hf of the row's metadata. Each lane reads the
-// row's 16 metadata bytes once (16 consecutive rows fill the 64 banks), keeps the two dwords of its
-// half, and every SMFMAC selects its index set by the instruction's key, so no per-lane shift of
-// the metadata is needed.
+// 8 metadata bytes of its half of the row once, and every SMFMAC selects its index set by the
+// instruction's key, so no per-lane shift or select of the metadata is needed.
 template <bool kSparseK, class E>
 __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const LaneOffsets &lo, int hf,
                                       const char *zp) {
@@ -228,8 +228,7 @@ __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const Lan
       for (int cc = 0; cc < 8; ++cc)
         acc = mfma32(as8<E>(k[cc]), half8<E>(w.qv[cc & 3], cc >> 2), acc);
     } else {
-      const uint4 m4 = lds16(st + lo.km + T * 512);
-      const uint2 meta = hf ? make_uint2(m4.z, m4.w) : make_uint2(m4.x, m4.y);
+      const uint2 meta = lds8(st + lo.km + T * 512);
       uint4 k[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) k[s] = lds16(st + (lo.kn ^ (16 * s)) + T * 4096);
@@ -252,7 +251,7 @@ __device__ __forceinline__ void gemm1(WaveState<E> &w, const char *st, const Lan
 // SMFMAC: one branch around the whole sequence makes the compiler copy the accumulators at the join.
 template <class E>
 __device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *st, bool sparse,
-                                                  const uint2 *meta, int u, const LaneOffsets &lo,
+                                                  const uint32_t *meta, int u, const LaneOffsets &lo,
                                                   int hf) {
   const int off = sparse ? (lo.vn ^ (32 * u)) : (lo.vd ^ (64 * u));
   uint4 v0[4], v1[4];
@@ -264,17 +263,23 @@ __device__ __forceinline__ void gemm2_smfmac_step(WaveState<E> &w, const char *s
   }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint32_t idx = (u ? meta[ct].y : meta[ct].x) >> (16 * hf);
-    w.o[ct] = smfmac32(as8<E>(v0[ct]), w.p[u], idx, w.o[ct]);
+    w.o[ct] = u ? smfmac32<E, 1>(as8<E>(v0[ct]), w.p[u], meta[ct], w.o[ct])
+                : smfmac32<E, 0>(as8<E>(v0[ct]), w.p[u], meta[ct], w.o[ct]);
     if (!sparse) w.o[ct] = smfmac32(as8<E>(v1[ct]), w.p[u], 0xEEEEu, w.o[ct]);
   }
 }
-// Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (table at didx).
-__device__ __forceinline__ void load_vmeta(uint2 *meta, const char *st, bool sparse,
+// Index words of GEMM2: a 2:4 tile's metadata, or the dense index words (table at didx). A
+// 32-channel tile's 8 bytes hold the 16-bit words of k-step 0 (both lane halves) and then those of
+// k-step 1; one byte permute per tile gathers the lane half's two words into one register, low
+// half k-step 0 and high half k-step 1, and each SMFMAC picks its half by the instruction's key.
+__device__ __forceinline__ void load_vmeta(uint32_t *meta, const char *st, bool sparse,
                                            const LaneOffsets &lo, const char *didx) {
   const char *base = sparse ? st : didx - kVMetaOff;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) meta[ct] = lds8(base + lo.vm + ct * 32 * 8);
+  for (int ct = 0; ct < 4; ++ct) {
+    const uint2 m = lds8(base + lo.vm + ct * 32 * 8);
+    meta[ct] = __builtin_amdgcn_perm(m.y, m.x, lo.vsel);
+  }
 }
 
 // ---- GEMM2 on the decompress path (dense operands), one 16-token k-step ks --------------------
@@ -379,7 +384,7 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
                                                float c, const char *didx) {
   float lsum = 0.f;
   const float mc = w.m_use == -INFINITY ? 0.f : w.m_use;  // rows with nothing visible yet
-  uint2 meta[4];
+  uint32_t meta[4];
   load_vmeta(meta, st_prev, gemm && sparse, lo, didx);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -394,7 +399,7 @@ __device__ __forceinline__ float exp_and_gemm2(WaveState<E> &w, const char *st_p
 // index words of both), and the SMFMACs of k-step u on them, so that the reads can be issued well
 // ahead of the SMFMACs.
 struct VOps {
-  uint2 meta[4];
+  uint32_t meta[4];
   uint4 v0[4], v1[4];
 };
 __device__ __forceinline__ void gemm2_read(VOps &v, const char *st, bool sparse, int u,
@@ -413,8 +418,8 @@ __device__ __forceinline__ void gemm2_apply(WaveState<E> &w, const VOps &v, bool
                                             int hf) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint32_t idx = (u ? v.meta[ct].y : v.meta[ct].x) >> (16 * hf);
-    w.o[ct] = smfmac32(as8<E>(v.v0[ct]), w.p[u], idx, w.o[ct]);
+    w.o[ct] = u ? smfmac32<E, 1>(as8<E>(v.v0[ct]), w.p[u], v.meta[ct], w.o[ct])
+                : smfmac32<E, 0>(as8<E>(v.v0[ct]), w.p[u], v.meta[ct], w.o[ct]);
     if (!sparse) w.o[ct] = smfmac32(as8<E>(v.v1[ct]), w.p[u], 0xEEEEu, w.o[ct]);
   }
 }
@@ -456,7 +461,7 @@ __device__ __forceinline__ void relayout_through_lds(WaveState<E> &w, int u, cha
 template <class E>
 __device__ __forceinline__ void gemm2_smfmac(WaveState<E> &w, const char *st, bool sparse,
                                              const LaneOffsets &lo, int hf, const char *didx) {
-  uint2 meta[4];
+  uint32_t meta[4];
   load_vmeta(meta, st, sparse, lo, didx);
 #pragma unroll
   for (int u = 0; u < 2; ++u) gemm2_smfmac_step(w, st, sparse, meta, u, lo, hf);
@@ -596,11 +601,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
     const int f16 = r & 15, f8 = (r >> 1) & 7, f4 = (r >> 2) & 3;
     lo.kd = r * 256 + 32 * (f16 >> 1) + 16 * (hf ^ (f16 & 1));
     lo.kn = r * 128 + 16 * ((4 * hf) ^ f8);
-    lo.km = kMetaOff + r * 16;
+    lo.km = kMetaOff + r * 16 + 8 * hf;
     lo.vd = kRegion + r * 128 + 16 * ((2 * hf) ^ f8);
     lo.vdd = kRegion + r * 128 + 32 * (f8 >> 1) + 16 * (hf ^ (f8 & 1));
     lo.vn = kRegion + r * 64 + 32 * (f4 >> 1) + 16 * (hf ^ (f4 & 1));
     lo.vm = kVMetaOff + r * 8;
+    lo.vsel = hf ? 0x07060302u : 0x05040100u;
   }
 
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
@@ -840,9 +846,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           gemm2_apply(w, v, sparse_v, 0, hf);
           gemm2_read(v, sv, sparse_v, 1, lo, didx);
           gemm2_apply(w, v, sparse_v, 1, hf);
-          stage ^= 1;
           kt0 = kt1;
           mk0 = mk1;
+          stage ^= 1;
           mv0 = mv1;
         }
       } else {
