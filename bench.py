@@ -717,6 +717,18 @@ def run_peaks(reps=3):
               "ms_both": round(res["both"] * 1e3, 4),
               "overlap": round((res["mfma_only"] + res["valu_only"] - res["both"])
                                / min(res["mfma_only"], res["valu_only"]), 3)})
+    # Matrix phase and dependent vector phase in turn in every wave, one or two waves per SIMD.
+    pit = 8192
+    for vr in (2, 4, 8):
+        for waves in (4, 8):
+            res = {tag: timed(lambda: pk.mix_phase(part, waves, pit, vr, grid, out, clk))
+                   for tag, part in (("matrix_only", 1), ("vector_only", 2), ("both", 0))}
+            emit({"peak": "mix_phase", "vector_rounds": vr, "waves_per_simd": waves // 4,
+                  "ms_matrix_only": round(res["matrix_only"] * 1e3, 4),
+                  "ms_vector_only": round(res["vector_only"] * 1e3, 4),
+                  "ms_both": round(res["both"] * 1e3, 4),
+                  "overlap": round((res["matrix_only"] + res["vector_only"] - res["both"])
+                                   / min(res["matrix_only"], res["vector_only"]), 3)})
     # LDS read bandwidth per CU (one workgroup per CU, 4 / 8 / 16 waves).
     for waves in (4, 8, 16):
         lit = 4096

@@ -74,6 +74,14 @@ int hsp_mix_wave(int op, int nops, int grid, int waves, int iters, float *out, u
 int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, float *out, uint64_t *clk,
                   void *stream);
 
+/* A tile of attention in miniature: every wave of a workgroup of 'waves' (4 or 8: one or two
+   per SIMD) runs 'iters' rounds of a matrix phase (eight v_mfma_f32_32x32x16_bf16 over four
+   accumulators) followed by a vector phase of 'vrounds' rounds over 8 chains (FMA and exponential
+   rounds in turn) that reads the matrix results, its bf16 pack being the next matrix phase's B
+   operand. 'part' 0 runs both phases, 1 the matrix phase only, 2 the vector phase only. */
+int hsp_mix_phase(int part, int waves, int iters, int vrounds, int grid, float *out, uint64_t *clk,
+                  void *stream);
+
 /* LDS read bandwidth: 'iters' rounds of eight ds_read_b128 per wave (1 KB of consecutive bytes
    each, conflict-free) in workgroups of 'waves' waves (1..16). */
 int hsp_lds_read(int grid, int waves, int iters, float *out, uint64_t *clk, void *stream);

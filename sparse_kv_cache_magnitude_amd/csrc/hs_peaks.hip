@@ -215,6 +215,52 @@ __global__ __launch_bounds__(512) void k_mix_split(float *out, int mfma_iters, i
   clock_mark(clk, 1);
 }
 
+// Each wave alternates a matrix phase (eight 32x32x16 MFMAs over four accumulators) and a vector
+// phase (8 chains, alternately FMA and exponential rounds) that depends on the matrix results,
+// whose bf16 pack feeds the next matrix phase, as a tile of attention does (GEMM, softmax, GEMM).
+// PART 0: both phases; 1: the matrix phase only; 2: the vector phase only.
+template <int PART>
+__global__ __launch_bounds__(512) void k_mix_phase(float *out, int iters, int vrounds, float c1,
+                                                   float c2, uint64_t *clk) {
+  __shared__ float pad[kPadFloats];
+  clock_mark(clk, 0);
+  const int t = threadIdx.x, tid = blockIdx.x * blockDim.x + t;
+  const uint4 a = seed4(t, 1);
+  uint4 b = seed4(t, 2);
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = zero16();
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.25f + 0.01f * (float)((t + j) & 15);
+  for (int i = 0; i < iters; ++i) {
+    if constexpr (PART != 2) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc[k & 3] = hs::mma32x16(hs::as8<__bf16>(a), hs::as8<__bf16>(b), acc[k & 3]);
+    }
+    if constexpr (PART != 1) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = fmaf(acc[c & 3][c], 1e-6f, x[c]);
+      for (int r = 0; r < vrounds; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          x[c] = (r & 1) ? __builtin_amdgcn_exp2f(-fabsf(x[c])) : fmaf(x[c], c1, c2);
+      b.x = hs::pack2<__bf16>(x[0], x[1]);
+      b.y = hs::pack2<__bf16>(x[2], x[3]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[tid] = through_lds(pad, s);
+  clock_mark(clk, 1);
+}
+
 // LDS read bandwidth: every wave streams ds_read_b128 over a 64 KB window (each wave instruction
 // reads 1 KB of consecutive bytes, conflict-free), eight reads in flight; the values are only
 // made live (an empty asm statement takes them), so no vector arithmetic shares the issue slots.
@@ -383,6 +429,19 @@ HSP_API int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, floa
     case HSP_VALU_DOT2: k_mix_split<HSP_VALU_DOT2><<<grid, 512, 0, s>>>(out, mfma_iters, valu_iters, c1, c2, clk); break;
     default: return -1;
   }
+  return status(hipGetLastError());
+}
+
+HSP_API int hsp_mix_phase(int part, int waves, int iters, int vrounds, int grid, float *out,
+                          uint64_t *clk, void *stream) {
+  if (!out || grid <= 0 || (waves != 4 && waves != 8) || iters < 0 || vrounds < 0 ||
+      part < 0 || part > 2)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const float c1 = 0.99990f, c2 = 1e-4f;
+  if (part == 0) k_mix_phase<0><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
+  if (part == 1) k_mix_phase<1><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
+  if (part == 2) k_mix_phase<2><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
   return status(hipGetLastError());
 }
 

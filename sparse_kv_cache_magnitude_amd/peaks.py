@@ -11,7 +11,8 @@ HSP_MFMA_32X32X16, HSP_SMFMAC_32X32X32, HSP_MFMA_16X16X32, HSP_SMFMAC_16X16X64 =
 HSP_VALU_EXP2, HSP_VALU_FMA, HSP_VALU_MAX3, HSP_VALU_CVT, HSP_VALU_SOFTMAX = 0, 1, 2, 3, 4
 HSP_VALU_DOT2 = 5
 
-EXPORTS = ("hsp_matrix_loop", "hsp_matrix_chain", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_lds_read",
+EXPORTS = ("hsp_matrix_loop", "hsp_matrix_chain", "hsp_valu_loop", "hsp_mix_wave", "hsp_mix_split", "hsp_mix_phase",
+           "hsp_lds_read",
            "hsp_read")
 
 _lib = None
@@ -30,6 +31,7 @@ def lib():
         L.hsp_valu_loop.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_wave.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_mix_split.argtypes = [I, I, I, I, P, P, P]
+        L.hsp_mix_phase.argtypes = [I, I, I, I, I, P, P, P]
         L.hsp_lds_read.argtypes = [I, I, I, P, P, P]
         L.hsp_read.argtypes = [I, P, ctypes.c_size_t, I, P, P]
         for f in EXPORTS:
@@ -72,6 +74,11 @@ def mix_wave(op, nops, grid, waves, iters, out, clk=None):
 def mix_split(op, mfma_iters, valu_iters, grid, out, clk=None):
     _check(lib().hsp_mix_split(op, mfma_iters, valu_iters, grid, _p(out), _p(clk), _s()),
            "mix_split")
+
+
+def mix_phase(part, waves, iters, vrounds, grid, out, clk=None):
+    _check(lib().hsp_mix_phase(part, waves, iters, vrounds, grid, _p(out), _p(clk), _s()),
+           "mix_phase")
 
 
 def lds_read(grid, waves, iters, out, clk=None):
