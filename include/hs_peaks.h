@@ -76,9 +76,10 @@ int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, float *out, 
 
 /* A tile of attention in miniature: every wave of a workgroup of 'waves' (4 or 8: one or two
    per SIMD) runs 'iters' rounds of a matrix phase (eight v_mfma_f32_32x32x16_bf16 over four
-   accumulators) followed by a vector phase of 'vrounds' rounds over 8 chains (FMA and exponential
-   rounds in turn) that reads the matrix results, its bf16 pack being the next matrix phase's B
-   operand. 'part' 0 runs both phases, 1 the matrix phase only, 2 the vector phase only. */
+   accumulators) followed by a vector phase of 'vrounds' (2, 4 or 8) rounds over 8 chains (FMA and
+   exponential rounds in turn) that reads the matrix results, its bf16 pack being the next matrix
+   phase's B operand. 'part' 0 runs both phases, 1 the matrix phase only, 2 the vector phase
+   only. */
 int hsp_mix_phase(int part, int waves, int iters, int vrounds, int grid, float *out, uint64_t *clk,
                   void *stream);
 

@@ -216,12 +216,12 @@ __global__ __launch_bounds__(512) void k_mix_split(float *out, int mfma_iters, i
 }
 
 // Each wave alternates a matrix phase (eight 32x32x16 MFMAs over four accumulators) and a vector
-// phase (8 chains, alternately FMA and exponential rounds) that depends on the matrix results,
-// whose bf16 pack feeds the next matrix phase, as a tile of attention does (GEMM, softmax, GEMM).
-// PART 0: both phases; 1: the matrix phase only; 2: the vector phase only.
-template <int PART>
-__global__ __launch_bounds__(512) void k_mix_phase(float *out, int iters, int vrounds, float c1,
-                                                   float c2, uint64_t *clk) {
+// phase (8 chains, VR / 2 pairs of an FMA round and an exponential round) that depends on the
+// matrix results, whose bf16 pack feeds the next matrix phase, as a tile of attention does (GEMM,
+// softmax, GEMM). PART 0: both phases; 1: the matrix phase only; 2: the vector phase only.
+template <int PART, int VR>
+__global__ __launch_bounds__(512) void k_mix_phase(float *out, int iters, float c1, float c2,
+                                                   uint64_t *clk) {
   __shared__ float pad[kPadFloats];
   clock_mark(clk, 0);
   const int t = threadIdx.x, tid = blockIdx.x * blockDim.x + t;
@@ -242,10 +242,13 @@ __global__ __launch_bounds__(512) void k_mix_phase(float *out, int iters, int vr
     if constexpr (PART != 1) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[c] = fmaf(acc[c & 3][c], 1e-6f, x[c]);
-      for (int r = 0; r < vrounds; ++r)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          x[c] = (r & 1) ? __builtin_amdgcn_exp2f(-fabsf(x[c])) : fmaf(x[c], c1, c2);
+      for (int r = 0; r < VR / 2; ++r) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = fmaf(x[c], c1, c2);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = __builtin_amdgcn_exp2f(-fabsf(x[c]));
+      }
       b.x = hs::pack2<__bf16>(x[0], x[1]);
       b.y = hs::pack2<__bf16>(x[2], x[3]);
     }
@@ -434,14 +437,23 @@ HSP_API int hsp_mix_split(int op, int mfma_iters, int valu_iters, int grid, floa
 
 HSP_API int hsp_mix_phase(int part, int waves, int iters, int vrounds, int grid, float *out,
                           uint64_t *clk, void *stream) {
-  if (!out || grid <= 0 || (waves != 4 && waves != 8) || iters < 0 || vrounds < 0 ||
-      part < 0 || part > 2)
+  if (!out || grid <= 0 || (waves != 4 && waves != 8) || iters < 0 || part < 0 || part > 2)
     return -1;
   hipStream_t s = (hipStream_t)stream;
   const float c1 = 0.99990f, c2 = 1e-4f;
-  if (part == 0) k_mix_phase<0><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
-  if (part == 1) k_mix_phase<1><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
-  if (part == 2) k_mix_phase<2><<<grid, 64 * waves, 0, s>>>(out, iters, vrounds, c1, c2, clk);
+  const dim3 g(grid), b(64 * waves);
+  switch (part * 16 + vrounds) {
+    case 2: k_mix_phase<0, 2><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 4: k_mix_phase<0, 4><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 8: k_mix_phase<0, 8><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 18: k_mix_phase<1, 2><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 20: k_mix_phase<1, 4><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 24: k_mix_phase<1, 8><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 34: k_mix_phase<2, 2><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 36: k_mix_phase<2, 4><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    case 40: k_mix_phase<2, 8><<<g, b, 0, s>>>(out, iters, c1, c2, clk); break;
+    default: return -1;
+  }
   return status(hipGetLastError());
 }
 
