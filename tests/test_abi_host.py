@@ -38,6 +38,18 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_peaks_library_exports_every_declared_symbol():
+    """The measurement library (include/hs_peaks.h): header, binding and exports agree."""
+    from sparse_kv_cache_magnitude_amd import peaks
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "hs_peaks.h")).read(),
+                 flags=re.S)
+    declared = sorted(set(re.findall(r"\b(hsp_[a-z_0-9]+)\s*\(", src)))
+    assert declared == sorted(peaks.EXPORTS)
+    lib = ctypes.CDLL(peaks.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
 @pytest.mark.parametrize("b,hq,hkv,L,B,counts", [
     (8, 32, 8, 32768, 64, (77, 307, 307)),
     (1, 32, 8, 16384, 128, (0, 90, 90)),
