@@ -229,7 +229,9 @@ __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t 
 }
 // N (1, 2 or 4) direct loads of one lane pattern: load i reads 16 bytes per lane at g[i] + voff
 // into LDS m0 + 1024-byte slot, m0 = lds0 + i * lstride. M0 is saved once and restored once for the
-// run (one load per M0 write, with the one wait state an M0 write needs before a direct load).
+// run (one load per M0 write, with the one wait state an M0 write needs before a direct load). The
+// M0 additions write SCC, so SCC is declared clobbered: a 64-bit address add split around the run
+// must not take its carry from them.
 template <int N>
 __device__ __forceinline__ void dma16_run(const char *const (&g)[N], uint32_t voff, uint32_t lds0,
                                           uint32_t lstride) {
@@ -243,7 +245,7 @@ __device__ __forceinline__ void dma16_run(const char *const (&g)[N], uint32_t vo
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(voff), "s"(lds0), "s"(g[0])
-        : "memory");
+        : "memory", "scc");
   } else if constexpr (N == 2) {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -256,7 +258,7 @@ __device__ __forceinline__ void dma16_run(const char *const (&g)[N], uint32_t vo
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(voff), "s"(lds0), "s"(lstride), "s"(g[0]), "s"(g[1])
-        : "memory");
+        : "memory", "scc");
   } else {
     static_assert(N == 4, "runs of 1, 2 or 4 loads");
     asm volatile(
@@ -276,7 +278,7 @@ __device__ __forceinline__ void dma16_run(const char *const (&g)[N], uint32_t vo
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(voff), "s"(lds0), "s"(lstride), "s"(g[0]), "s"(g[1]), "s"(g[2]), "s"(g[3])
-        : "memory");
+        : "memory", "scc");
   }
 }
 

@@ -664,7 +664,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
     const uint32_t kl = lds_base + stage * L::kStride, vl = kl + kRegion;
     const uint32_t ksl = kl + SP, vsl = vl + SP;  // 2:4 buffers
     const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
-    if (mk > 0) {
+    if (__builtin_expect(mk > 0, 0)) {  // 2:4 tiles are the common case
       const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
       const uint32_t o = sp ? oKd[1] : oKd[0];
       const char *gr[16 / W];
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       if (wave == 1)
         dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], ksl + kMetaOff);
     }
-    if (mv > 0) {
+    if (__builtin_expect(mv > 0, 0)) {
       const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
       const char *gr[16 / W];
 #pragma unroll
