@@ -659,13 +659,21 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
   const uint16_t *vd_h = a.c.v_dense + (size_t)head * a.ndv * B * kD;
   const uint16_t *vn_h = a.c.v_nnz + (size_t)head * a.nsv * B * (kD / 2);
   const uint16_t *vm_h = a.c.v_meta + (size_t)head * a.nsv * B * (kD / 16);
-  auto issue = [&](int kt, int mk, int mv, int stage) {
+  // Byte address of element e of a per-head array. A head holds at most kMaxBlocks blocks of at
+  // most 128 x 128 elements, so 2 e fits 32 unsigned bits: one 32-bit shift, one 64-bit add.
+  auto elem_at = [](const uint16_t *base, int e) __attribute__((always_inline)) {
+    return reinterpret_cast<const char *>(base) + (uint32_t)e * 2u;
+  };
+  auto issue = [&](int kt, int mk, int mv, int stage, auto kind_tag) {
+    constexpr int KIND = decltype(kind_tag)::value;
     const int half = kt % TPB;
     const uint32_t kl = lds_base + stage * L::kStride, vl = kl + kRegion;
     const uint32_t ksl = kl + SP, vsl = vl + SP;  // 2:4 buffers
     const int sp = (kSmfmac && mv > 0) ? 1 : 0;  // GEMM1 row order of this tile (see tau)
-    if (__builtin_expect(mk > 0, 0)) {  // 2:4 tiles are the common case
-      const char *g = uniform_ptr(kd_h + ((mk - 1) * B + kTile * half) * kD);
+    // The kinds are constants on the specialised walks; on the general one 2:4 tiles are the
+    // common case.
+    if (KIND == 2 || (KIND == 0 && __builtin_expect(mk > 0, 0))) {
+      const char *g = uniform_ptr(elem_at(kd_h, ((mk - 1) * B + kTile * half) * kD));
       const uint32_t o = sp ? oKd[1] : oKd[0];
       const char *gr[16 / W];
 #pragma unroll
@@ -673,24 +681,24 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       dma16_run<16 / W>(gr, o, kl + 1024 * wave, 1024 * W);
     } else {
       const int row0 = (-mk - 1) * B + kTile * half;
-      const char *g = uniform_ptr(kn_h + row0 * (kD / 2));
+      const char *g = uniform_ptr(elem_at(kn_h, row0 * (kD / 2)));
       const uint32_t o = sp ? oKn[1] : oKn[0];
       const char *gs[8 / W];
 #pragma unroll
       for (int i = 0; i < 8 / W; ++i) gs[i] = g + i * (8 * W) * kD;
       dma16_run<8 / W>(gs, o, ksl + 1024 * wave, 1024 * W);
       if (wave == 1)
-        dma16(uniform_ptr(km_h + row0 * (kD / 16)), sp ? oKm[1] : oKm[0], ksl + kMetaOff);
+        dma16(uniform_ptr(elem_at(km_h, row0 * (kD / 16))), sp ? oKm[1] : oKm[0], ksl + kMetaOff);
     }
-    if (__builtin_expect(mv > 0, 0)) {
-      const char *g = uniform_ptr(vd_h + (mv - 1) * B * kD + kTile * half);
+    if (KIND == 2 || (KIND == 0 && __builtin_expect(mv > 0, 0))) {
+      const char *g = uniform_ptr(elem_at(vd_h, (mv - 1) * B * kD + kTile * half));
       const char *gr[16 / W];
 #pragma unroll
       for (int i = 0; i < 16 / W; ++i) gr[i] = g + i * (8 * W) * 2 * B;
       dma16_run<16 / W>(gr, oVd, vl + 1024 * wave, 1024 * W);
     } else {
       const int blk = (-mv - 1) * B * kD;
-      const char *g = uniform_ptr(vn_h + blk / 2 + (kTile / 2) * half);
+      const char *g = uniform_ptr(elem_at(vn_h, blk / 2 + (kTile / 2) * half));
       // 16 rows per load; load q = wave + W i covers rows 16 q .., and rows 32 ct + .. start at
       // ct * kCtStride: LDS offset (q >> 1) kCtStride + 1024 (q & 1), a step of W / 2 groups per i.
       const char *gs[8 / W];
@@ -698,7 +706,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       for (int i = 0; i < 8 / W; ++i) gs[i] = g + i * (16 * W) * B;
       dma16_run<8 / W>(gs, oVn, vsl + (wave >> 1) * kCtStride + 1024 * (wave & 1),
                        (W / 2) * kCtStride);
-      const char *gm = uniform_ptr(vm_h + blk / 16 + (kTile / 16) * half);
+      const char *gm = uniform_ptr(elem_at(vm_h, blk / 16 + (kTile / 16) * half));
       if (B == 64) {
         if (wave == 2) dma16(gm, oVm, ksl + kVMetaOff);
       } else if (wave >= kVmWave0 && wave < kVmWave0 + 4) {
@@ -712,7 +720,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
   int kt0 = 0, mk0 = 0, mv0 = 0;
   if (n_tiles > 0) {
     tile_info(0, kt0, mk0, mv0);
-    issue(kt0, mk0, mv0, 0);
+    issue(kt0, mk0, mv0, 0, std::integral_constant<int, 0>{});
   }
 
   // Every wave walks every tile the workgroup stages (uniform control flow); tiles beyond a wave's
@@ -729,7 +737,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
       const int next_stage = stage == NS - 1 ? 0 : stage + 1;
       wait_vmem(0);  // this wave's loads of tile it have landed
       barrier();     // ... and every wave's; the scratch tile of tile it - 1 is no longer read
-      if (more) issue(kt1, mk1, mv1, next_stage);
+      if (more) issue(kt1, mk1, mv1, next_stage, std::integral_constant<int, 0>{});
 
       const char *st = lds + stage * L::kStride;
       const bool sparse_k = mk0 < 0, sparse_v = mv0 < 0;
@@ -816,13 +824,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           if (more) tile_info(it + 1, kt1, mk1, mv1);
           if constexpr ((A & kAblSyncLoads) != 0) {
             // ablation: the tile's own loads, waited for at once (no overlap with computing)
-            if (it > 0) issue(kt0, mk0, mv0, stage);
+            if (it > 0) issue(kt0, mk0, mv0, stage, kind_tag);
             wait_vmem(0);
             barrier();
           } else {
             wait_vmem(0);  // this wave's loads of tile it have landed
             barrier();     // ... and every wave's; the other stage (tile it - 1) is no longer read
-            if (more) issue(kt1, mk1, mv1, stage ^ 1);
+            if (more) issue(kt1, mk1, mv1, stage ^ 1, kind_tag);
           }
           const char *st = lds + stage * L::kStride;
           bool sparse_k, sparse_v;
@@ -864,7 +872,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_prefill(PrefillArgs 
           const int next_stage = stage == NS - 1 ? 0 : stage + 1;
           wait_vmem(0);  // this wave's loads of tile it have landed
           barrier();     // ... and every wave's; stage next_stage (tile it - 2) is no longer read
-          if (more) issue(kt1, mk1, mv1, next_stage);
+          if (more) issue(kt1, mk1, mv1, next_stage, kind_tag);
           const char *st = lds + stage * L::kStride;
           bool sparse_k, sparse_v;
           kinds_of(mk0, mv0, sparse_k, sparse_v);
